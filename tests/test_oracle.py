@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a hand-built golden block, a
+closed form, exact rational brute force, a library routine (numpy's fp16
+conversion, float64 matmul), integer arithmetic, or an invariant of the
+definition.  Runs on the CPU only.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from outer_product_gemm_amd import synth
+from tests import quant_pack as qp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    raw, vals = [], {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#"):
+                continue
+            if parts[0] == "hex":
+                raw += [int(x, 16) for x in parts[1:]]
+            elif parts[0] == "val":
+                v = parts[2]
+                vals[int(parts[1])] = float.fromhex(v) if "0x" in v else float(v)
+    return np.array(raw, dtype=np.uint8), vals
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_golden_q4_K_block():
+    """Hand-built q4_K block: every 6-bit scale/min position and both nibbles."""
+    raw, vals = _read_golden("q4_K_block_hand.txt")
+    assert raw.size == 144
+    x = oracle.dequant_rows(raw, oracle.Q4_K, 256, 1, 144)[0]
+    for idx, v in vals.items():
+        assert x[idx] == np.float32(v), (idx, x[idx], v)
+
+
+def test_golden_q8_0_blocks():
+    """Hand-built q8_0 blocks, including a subnormal fp16 scale."""
+    raw, vals = _read_golden("q8_0_block_hand.txt")
+    assert raw.size == 68
+    x = oracle.dequant_rows(raw, oracle.Q8_0, 64, 1, 68)[0]
+    for idx, v in vals.items():
+        assert x[idx] == np.float32(v), (idx, x[idx], v)
+
+
+def test_fp16_decoder_all_finite_patterns():
+    """The oracle's fp16 decoder against numpy's binary16 conversion, for all
+    63,488 finite bit patterns (normal, subnormal, +-0).  Decoded through
+    q8_0 blocks with q = 1 and q = -1, so x = +-d exactly."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = bits[np.isfinite(bits.view(np.float16))]
+    nblk = finite.size
+    rows = np.zeros((nblk, 34), dtype=np.uint8)
+    rows[:, 0:2] = finite.reshape(-1, 1).view(np.uint8).reshape(-1, 2)
+    q = np.array([1, -1] * 16, dtype=np.int8)
+    rows[:, 2:] = q.view(np.uint8)
+    x = oracle.dequant_rows(rows.reshape(1, -1), oracle.Q8_0, 32 * nblk, 1, 34 * nblk)[0]
+    x = x.reshape(nblk, 32)
+    expect = finite.view(np.float16).astype(np.float32)
+    assert np.array_equal(x[:, 0].view(np.uint32), expect.view(np.uint32))
+    assert np.array_equal(x[:, 1], -expect)
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00])
+def test_fp16_decoder_refuses_inf_nan(bad):
+    rows = np.zeros((1, 34), dtype=np.uint8)
+    rows[0, 0:2] = np.array([bad], dtype=np.uint16).view(np.uint8)
+    with pytest.raises(ValueError):
+        oracle.dequant_rows(rows, oracle.Q8_0, 32, 1, 34)
+
+
+def test_q8_0_random_blocks_exact():
+    """q8_0 values from packed fields: d*q, exact (<= 18 significant bits)."""
+    rng = np.random.default_rng(101)
+    for _ in range(20):
+        d_bits = qp.half_bits(rng.uniform(1e-3, 1e-2)) if rng.random() < .5 else int(rng.integers(0, 0x7C00))
+        q = rng.integers(-128, 128, size=32)
+        blk = np.frombuffer(qp.pack_q8_0(d_bits, q), dtype=np.uint8)
+        x = oracle.dequant_rows(blk, oracle.Q8_0, 32, 1, 34)[0]
+        assert np.array_equal(x, qp.to_f32(qp.q8_0_values(d_bits, q)))
+
+
+def test_q4_K_random_blocks_exact():
+    """q4_K from packed fields, all 6-bit scale/min values and codes random;
+    expected = single rounding of the exact d*sc*q - dmin*m."""
+    rng = np.random.default_rng(102)
+    for t in range(40):
+        if t % 4 == 0:   # subnormal or tiny scales as well
+            d_bits, dmin_bits = int(rng.integers(1, 0x0400)), int(rng.integers(0, 0x0400))
+        else:
+            d_bits = int(rng.integers(0, 0x7C00))
+            dmin_bits = int(rng.integers(0, 0x7C00))
+        sc = rng.integers(0, 64, size=8)
+        m = rng.integers(0, 64, size=8)
+        q = rng.integers(0, 16, size=256)
+        blk = np.frombuffer(qp.pack_q4_K(d_bits, dmin_bits, sc, m, q), dtype=np.uint8)
+        x = oracle.dequant_rows(blk, oracle.Q4_K, 256, 1, 144)[0]
+        expect = qp.to_f32(qp.q4_K_values(d_bits, dmin_bits, sc, m, q))
+        assert np.array_equal(x.view(np.uint32), expect.view(np.uint32)) or np.array_equal(x, expect)
+
+
+def test_q4_K_single_field_isolation():
+    """Each sub-block j alone gets a nonzero scale (then a nonzero min): only
+    its 32 values may change.  Pins which 6-bit field belongs to which j."""
+    one = qp.half_bits(1.0)
+    q = [(e * 7 + 3) % 16 for e in range(256)]
+    for j in range(8):
+        for which in ("sc", "m"):
+            sc = [0] * 8
+            m = [0] * 8
+            (sc if which == "sc" else m)[j] = 37 + j   # high bits set: 37..44 >= 32
+            blk = np.frombuffer(qp.pack_q4_K(one, one, sc, m, q), dtype=np.uint8)
+            x = oracle.dequant_rows(blk, oracle.Q4_K, 256, 1, 144)[0]
+            for e in range(256):
+                if e // 32 != j:
+                    assert x[e] == 0.0
+                elif which == "sc":
+                    assert x[e] == (37 + j) * q[e]
+                else:
+                    assert x[e] == -(37 + j)
+
+
+# ---------------------------------------------------------------- contraction
+
+def _f32_instance(rng, ne00, K, ne02, ne03, ne10, ne12, ne13, scale=1.0):
+    a = (rng.standard_normal((ne03, ne02, K, ne00)) * scale).astype(np.float32)
+    b = rng.standard_normal((ne13, ne12, K, ne10)).astype(np.float32)
+    ne, nb = synth.make_ne_nb(synth.F32, (ne00, K, ne02, ne03), (ne10, K, ne12, ne13))
+    return a, b, ne, nb
+
+
+def test_rank1_closed_form_K1():
+    """K = 1: dst = a[i0]*b[i1], the exact rank-1 outer product."""
+    rng = np.random.default_rng(7)
+    a, b, ne, nb = _f32_instance(rng, 13, 1, 1, 1, 29, 1, 1)
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    expect = b[0, 0, 0, :].astype(np.float64)[:, None] * a[0, 0, 0, :].astype(np.float64)[None, :]
+    assert np.array_equal(ref[0, 0], expect)
+    assert np.array_equal(den[0, 0], np.abs(expect))
+
+
+def _brute_force(avals, bvals, ne):
+    """Exact rational OUT_PROD straight from the definition (tiny shapes).
+    avals[i03][i02][k][i0] and bvals[i3][i2][k][i1] are float arrays."""
+    ne00, K, ne02, ne03, ne10, _, ne12, ne13 = ne[:8]
+    dps2, dps3 = ne12 // ne02, ne13 // ne03
+    out = np.zeros((ne13, ne12, ne10, ne00), dtype=object)
+    dn = np.zeros((ne13, ne12, ne10, ne00), dtype=object)
+    for i3 in range(ne13):
+        for i2 in range(ne12):
+            for i1 in range(ne10):
+                for i0 in range(ne00):
+                    s = Fraction(0)
+                    t = Fraction(0)
+                    for k in range(K):
+                        x = Fraction(float(avals[i3 // dps3][i2 // dps2][k][i0]))
+                        y = Fraction(float(bvals[i3][i2][k][i1]))
+                        s += x * y
+                        t += abs(x) * abs(y)
+                    out[i3, i2, i1, i0] = s
+                    dn[i3, i2, i1, i0] = t
+    return out, dn
+
+
+def _assert_close_to_exact(ref, den, exact, exact_den, rel=1e-15):
+    for idx in np.ndindex(ref.shape):
+        e = exact[idx]
+        assert abs(Fraction(float(ref[idx])) - e) <= Fraction(rel) * exact_den[idx] + Fraction(0), idx
+        assert abs(Fraction(float(den[idx])) - exact_den[idx]) <= Fraction(rel) * exact_den[idx]
+
+
+@pytest.mark.parametrize("shape", [
+    (3, 5, 1, 1, 4, 1, 1),
+    (5, 7, 2, 1, 3, 4, 1),     # dps2 = 2
+    (2, 6, 1, 2, 3, 3, 4),     # dps2 = 3, dps3 = 2
+    (4, 4, 3, 1, 2, 3, 1),     # ne12 == ne02: no broadcast
+    (3, 4, 2, 2, 3, 4, 4),     # dps2 = 2, dps3 = 2, both a dims > 1
+])
+def test_brute_force_rational_f32(shape):
+    """Exact rational brute force with broadcast on tiny shapes: pins indexing,
+    the i2/dps2 block broadcast (not modulo) and the double accumulation."""
+    ne00, K, ne02, ne03, ne10, ne12, ne13 = shape
+    rng = np.random.default_rng(sum(shape))
+    a, b, ne, nb = _f32_instance(rng, ne00, K, ne02, ne03, ne10, ne12, ne13)
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    exact, exact_den = _brute_force(a, b, ne)
+    _assert_close_to_exact(ref, den, exact, exact_den)
+
+
+def test_brute_force_rational_strided_views():
+    """Non-contiguous a and b (padded rows, padded and reversed-order slices):
+    the oracle must follow nb byte strides, not assume contiguity."""
+    rng = np.random.default_rng(11)
+    ne00, K, ne02, ne03, ne10, ne12, ne13 = 3, 4, 2, 1, 5, 4, 1
+    # a lives in a larger buffer: rows padded to 7 floats, slices 40 floats apart
+    abuf = rng.standard_normal(7 * 4 * 10 + 100).astype(np.float32)
+    bbuf = rng.standard_normal(9 * 4 * 4 * 2 + 200).astype(np.float32)
+    nb = [4, 28, 160, 320, 4, 36, 36 * 4 * 2, 36 * 4 * 2 * 4, 4, 12, 60, 240]
+    ne = [ne00, K, ne02, ne03, ne10, K, ne12, ne13, ne00, ne10, ne12, ne13]
+    ref, den = oracle.out_prod(abuf, oracle.F32, bbuf, ne, nb)
+
+    def A(i0, k, i02, i03):
+        return abuf[(i0 * 4 + k * 28 + i02 * 160 + i03 * 320) // 4]
+
+    def B(i1, k, i2, i3):
+        return bbuf[(i1 * 4 + k * 36 + i2 * 288 + i3 * 1152) // 4]
+    av = [[[[A(i0, k, i02, i03) for i0 in range(ne00)] for k in range(K)] for i02 in range(ne02)]
+          for i03 in range(ne03)]
+    bv = [[[[B(i1, k, i2, i3) for i1 in range(ne10)] for k in range(K)] for i2 in range(ne12)]
+          for i3 in range(ne13)]
+    exact, exact_den = _brute_force(av, bv, ne)
+    _assert_close_to_exact(ref, den, exact, exact_den)
+
+
+@pytest.mark.parametrize("a_type", [oracle.Q8_0, oracle.Q4_K])
+def test_brute_force_rational_quant(a_type):
+    """Quantized a on a tiny shape with broadcast: expected values from the
+    packed fields (exact rationals), contraction by brute force."""
+    rng = np.random.default_rng(12 + a_type)
+    qk = 32 if a_type == oracle.Q8_0 else 256
+    ne00, K, ne02, ne10, ne12 = qk, 3, 2, 2, 4
+    rows, vals = [], []
+    for _ in range(ne02 * K):
+        if a_type == oracle.Q8_0:
+            d = qp.half_bits(rng.uniform(1e-3, 1e-2))
+            q = rng.integers(-127, 128, size=32)
+            rows.append(qp.pack_q8_0(d, q))
+            vals.append(qp.q8_0_values(d, q))
+        else:
+            d = qp.half_bits(rng.uniform(1e-3, 1e-2))
+            dm = qp.half_bits(rng.uniform(1e-3, 1e-2))
+            sc, m, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 16, 256)
+            rows.append(qp.pack_q4_K(d, dm, sc, m, q))
+            vals.append(qp.q4_K_values(d, dm, sc, m, q))
+    a = np.frombuffer(b"".join(rows), dtype=np.uint8)
+    b = rng.standard_normal((1, ne12, K, ne10)).astype(np.float32)
+    ne, nb = synth.make_ne_nb(a_type, (ne00, K, ne02, 1), (ne10, K, ne12, 1))
+    ref, den = oracle.out_prod(a, a_type, b, ne, nb)
+    av = np.array([qp.to_f32(v) for v in vals]).reshape(1, ne02, K, ne00)
+    exact, exact_den = _brute_force(av, b, ne)
+    _assert_close_to_exact(ref, den, exact, exact_den)
+
+
+def test_matches_float64_matmul():
+    """Special case with no broadcast: numpy float64 matmul (BLAS dgemm)."""
+    rng = np.random.default_rng(5)
+    a, b, ne, nb = _f32_instance(rng, 37, 300, 1, 1, 53, 1, 1)
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    A = a[0, 0].astype(np.float64)   # (K, ne00)
+    B = b[0, 0].astype(np.float64)   # (K, ne10)
+    expect = B.T @ A                 # (ne10, ne00)
+    assert np.all(np.abs(ref[0, 0] - expect) <= 1e-13 * den[0, 0])
+    assert np.allclose(den[0, 0], np.abs(B).T @ np.abs(A), rtol=1e-13, atol=0)
+
+
+def test_integer_exact():
+    """Integer-valued inputs: every partial sum is an exact integer, so the
+    result must equal int64 arithmetic exactly, at a long K."""
+    rng = np.random.default_rng(6)
+    K = 4096
+    a = rng.integers(-16, 17, size=(1, 2, K, 9)).astype(np.float32)
+    b = rng.integers(-16, 17, size=(1, 6, K, 11)).astype(np.float32)
+    ne, nb = synth.make_ne_nb(synth.F32, (9, K, 2, 1), (11, K, 6, 1))
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    ai = a.astype(np.int64)
+    bi = b.astype(np.int64)
+    for i2 in range(6):
+        e = bi[0, i2].T @ ai[0, i2 // 3]
+        assert np.array_equal(ref[0, i2], e.astype(np.float64))
+        assert np.array_equal(den[0, i2], (np.abs(bi[0, i2]).T @ np.abs(ai[0, i2 // 3])).astype(np.float64))
+
+
+def test_broadcast_invariant():
+    """Slices sharing i2/dps2 with identical b slices are identical, and each
+    slice equals a separate one-slice call on (a[:,:,i2/dps2], b[:,:,i2])."""
+    rng = np.random.default_rng(8)
+    ne00, K, ne02, ne10, ne12 = 6, 33, 3, 7, 12
+    a, b, ne, nb = _f32_instance(rng, ne00, K, ne02, 1, ne10, ne12, 1)
+    b[0, 5] = b[0, 4]                       # 4 and 5 share i2/dps2 = 1
+    ref, _ = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    assert np.array_equal(ref[0, 4], ref[0, 5])
+    b[0, 8] = b[0, 4]                       # 8 belongs to another a slice
+    ref, _ = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    assert not np.array_equal(ref[0, 4], ref[0, 8])
+    ne1, nb1 = synth.make_ne_nb(synth.F32, (ne00, K, 1, 1), (ne10, K, 1, 1))
+    for i2 in range(ne12):
+        r1, _ = oracle.out_prod(np.ascontiguousarray(a[:, i2 // 4]), oracle.F32,
+                                np.ascontiguousarray(b[:, i2]), ne1, nb1)
+        assert np.array_equal(r1[0, 0], ref[0, i2])
+
+
+def test_transpose_symmetry_and_power_of_two_scaling():
+    """out_prod(a,b)[i0,i1] == out_prod(b,a)[i1,i0] (same products, same order)
+    and out_prod(a, 2^p b) == 2^p out_prod(a, b), both exactly."""
+    rng = np.random.default_rng(9)
+    a, b, ne, nb = _f32_instance(rng, 5, 70, 1, 1, 8, 1, 1)
+    ref, _ = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    ne_t, nb_t = synth.make_ne_nb(synth.F32, (8, 70, 1, 1), (5, 70, 1, 1))
+    ref_t, _ = oracle.out_prod(b, oracle.F32, a, ne_t, nb_t)
+    assert np.array_equal(ref[0, 0], ref_t[0, 0].T)
+    ref8, _ = oracle.out_prod(a, oracle.F32, b * np.float32(8.0), ne, nb)
+    assert np.array_equal(ref8, ref * 8.0)
+
+
+def test_sampled_columns_match_full():
+    rng = np.random.default_rng(10)
+    a, b, ne, nb = _f32_instance(rng, 9, 40, 2, 1, 12, 4, 1)
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    cols = np.array([[3, 0, 0], [11, 3, 0], [0, 2, 0]])
+    r, d = oracle.out_prod(a, oracle.F32, b, ne, nb, cols=cols)
+    for j, (i1, i2, i3) in enumerate(cols):
+        assert np.array_equal(r[j], ref[i3, i2, i1])
+        assert np.array_equal(d[j], den[i3, i2, i1])
+
+
+def test_empty_K_gives_zeros():
+    ne, nb = synth.make_ne_nb(synth.F32, (4, 0, 1, 1), (3, 0, 1, 1))
+    ref, den = oracle.out_prod(np.zeros(0, np.float32), oracle.F32, np.zeros(0, np.float32), ne, nb)
+    assert ref.shape == (1, 1, 3, 4) and not ref.any() and not den.any()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(k_mismatch=True), dict(bcast=True), dict(dst=True), dict(qk=True)])
+def test_oracle_refuses_contract_violations(bad):
+    ne, nb = synth.make_ne_nb(synth.F32, (4, 5, 2, 1), (3, 5, 4, 1))
+    a_type = oracle.F32
+    if "k_mismatch" in bad:
+        ne[5] = 6
+    if "bcast" in bad:
+        ne[6] = ne[10] = 3
+    if "dst" in bad:
+        ne[8] = 5
+    if "qk" in bad:
+        a_type = oracle.Q8_0
+    with pytest.raises(ValueError):
+        oracle.out_prod(np.zeros(64, np.float32), a_type, np.zeros(64, np.float32), ne, nb)
+
+
+# ---------------------------------------------------------------- the gate
+
+def test_gate_rejects_half_staging():
+    """Known-positive gate: the grouped-head broadcast workload (gradients past
+    65504) computed through half-precision staging must FAIL the checker, as
+    the pages' half-staged kernel failed their gradient-range test."""
+    inst = synth.workload("deltanet_bcast")
+    ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
+    a16 = inst.a.astype(np.float16).astype(np.float32)
+    b16 = inst.b.astype(np.float16).astype(np.float32)   # outliers become +-inf
+    assert np.isinf(b16).any()
+    with np.errstate(invalid="ignore", over="ignore"):
+        half = np.stack([np.stack([b16[0, i2].T @ a16[0, i2 // 4] for i2 in range(16)])])
+    res = oracle.check(half, ref, den)
+    assert not res["ok"] and res["n_nonfinite"] > 0
+    # and a float32 computation of the same thing passes
+    f32 = np.stack([np.stack([inst.b[0, i2].T @ inst.a[0, i2 // 4] for i2 in range(16)])])
+    assert oracle.check(f32, ref, den)["ok"]
+
+
+def test_gate_rejects_half_rounding_without_overflow():
+    """Inputs inside half's range but rounded to half (the pages' ~1e-3
+    relative damage) still fail the 1e-5 gate."""
+    rng = np.random.default_rng(3)
+    a, b, ne, nb = _f32_instance(rng, 16, 256, 1, 1, 32, 1, 1)
+    ref, den = oracle.out_prod(a, oracle.F32, b, ne, nb)
+    half = b[0, 0].astype(np.float16).astype(np.float32).T @ a[0, 0].astype(np.float16).astype(np.float32)
+    assert not oracle.check(half[None, None], ref, den)["ok"]
+
+
+def test_gate_semantics():
+    ref = np.array([1.0, 0.0, -2.0])
+    den = np.array([10.0, 0.0, 4.0])
+    assert oracle.check(np.array([1.0 + 9e-5, 0.0, -2.0]), ref, den)["ok"]
+    assert not oracle.check(np.array([1.0 + 2e-4, 0.0, -2.0]), ref, den)["ok"]
+    assert not oracle.check(np.array([1.0, 1e-30, -2.0]), ref, den)["ok"]   # den 0 => exact 0
+    assert not oracle.check(np.array([np.nan, 0.0, -2.0]), ref, den)["ok"]
+    assert not oracle.check(np.array([1.0, 0.0, np.inf]), ref, den)["ok"]
