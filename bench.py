@@ -1,0 +1,282 @@
+"""OUT_PROD throughput on one MI355X, with roofline and CPU-oracle baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+every launch of the workload (the default workload, the 27B q4_K weight x f32
+gradient products in both orientations, is two launches: m5120 k17408 n1024
+and m17408 k5120 n1024).  Inputs are resident in HBM before timing starts;
+R copies of them rotate so that consecutive steps do not hit the 256 MB
+Infinity Cache.  Timing: HIP events on the stream the kernels are launched on
+(torch's current stream), W untimed warmup steps, then exactly K timed steps
+between two synchronizations.
+
+Prints ONE JSON line (progress goes to stderr).  ``value`` is GFLOP/s of the
+whole step; ``roofline`` reports the dominant kernel's algorithmic rate per
+launch against the MI355X peak (fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s);
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from outer_product_gemm_amd import synth  # noqa: E402
+
+METRIC = "OUT_PROD GFLOP/s and GB/s vs roofline, LoRA-backward shapes, 1×MI355X"
+PEAK_MFMA_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+RIDGE = PEAK_MFMA_F32_TFLOPS * 1e3 / PEAK_HBM_GBPS   # flop per byte
+
+COMPOSITE = {
+    "q4_K_27B_both": ["q4_K_5120x17408", "q4_K_17408x5120"],
+}
+DEFAULT_WORKLOAD = "q4_K_27B_both"
+
+# The pages' per-op float-staging times for the same q4_K x f32 shapes
+# (Apple M5, Metal; "metal: OUT_PROD multiplies in float staging", review
+# answer on cost): midpoints of 88-94 ms and 88-90 ms.  Another machine:
+# context for vs_baseline only.
+PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0}
+
+# HBM traffic per launch from rocprofv3 PMC runs (FETCH_SIZE + WRITE_SIZE,
+# scaled by the copy-kernel calibration), keyed by workload, valid only for
+# the kernel sources whose hash is recorded with it.
+MEASURED_TRAFFIC = {}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "outer_product_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(inst):
+    """flops and bytes of one launch: 2*ne00*ne10*K*slices; unique a at its
+    stored size (a broadcast a slice counts once) + b + one dst write."""
+    ne = inst.ne
+    slices = ne[10] * ne[11]
+    flops = 2 * ne[0] * ne[4] * ne[1] * slices
+    a_bytes = synth.row_bytes(inst.a_type, ne[0]) * ne[1] * ne[2] * ne[3]
+    b_bytes = 4 * ne[4] * ne[1] * ne[6] * ne[7]
+    d_bytes = 4 * ne[0] * ne[4] * slices
+    return flops, a_bytes + b_bytes + d_bytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(list(synth.WORKLOADS) + list(COMPOSITE)))
+    ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for 600 MB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU-oracle time for the baseline sample (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from outer_product_gemm_amd import binding as B
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    B.load_library()
+    dev = torch.device("cuda:0")
+    names = COMPOSITE.get(args.workload, [args.workload])
+    log("workload", args.workload, names)
+
+    insts = [synth.workload(n) for n in names]
+    work = [algorithmic(i) for i in insts]
+    flops_step = sum(w[0] for w in work)
+    bytes_step = sum(w[1] for w in work)
+    set_bytes = sum(i.a.nbytes + i.b.nbytes + 4 * int(np.prod(i.dst_shape)) for i in insts)
+    R = args.rotate or max(1, min(8, int(np.ceil(600e6 / set_bytes))))
+
+    sets = []
+    for r in range(R):
+        bufs = []
+        for inst in insts:
+            a_d = torch.from_numpy(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1)).to(dev)
+            b_d = torch.from_numpy(inst.b).to(dev)
+            d_d = torch.empty(inst.dst_shape, dtype=torch.float32, device=dev)
+            plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(),
+                                   inst.ne, inst.nb)
+            bufs.append((a_d, b_d, d_d, plan))
+        sets.append(bufs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    log("rotating sets", R, "set MB %.1f" % (set_bytes / 1e6),
+        "plans", [(p[3]["kernel_name"], p[3]["tile_m"], p[3]["tile_n"], p[3]["grid"]) for p in sets[0]])
+
+    def launch(r, j):
+        inst = insts[j]
+        a_d, b_d, d_d, _ = sets[r][j]
+        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb, sptr)
+
+    for s in range(args.warmup):
+        for j in range(len(insts)):
+            launch(s % R, j)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in insts] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(K):
+        for j in range(len(insts)):
+            ev[s][j][0].record(stream)
+            launch(s % R, j)
+            ev[s][j][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / K
+    per_launch = np.array([[ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(insts))]
+                           for s in range(K)])  # ms
+    log("timed %d steps: %.4f ms/step (host wall %.3f s)" % (K, ms_step, wall))
+
+    # dominant kernel: all launches of a workload run one kernel family
+    avg_ms = per_launch.mean(axis=0)
+    flops_launch = np.array([w[0] for w in work], dtype=np.float64)
+    bytes_launch = np.array([w[1] for w in work], dtype=np.float64)
+    ai = flops_step / bytes_step
+    bound = "mfma" if ai >= RIDGE else "hbm"
+    kernels = sorted(set(p[3]["kernel_name"] for p in sets[0]))
+    if bound == "mfma":
+        achieved = float(np.mean(flops_launch / (avg_ms * 1e-3)) / 1e12)
+        peak, unit = PEAK_MFMA_F32_TFLOPS, "TFLOP/s"
+    else:
+        achieved = float(np.mean(bytes_launch / (avg_ms * 1e-3)) / 1e9)
+        peak, unit = PEAK_HBM_GBPS, "GB/s"
+    src_hash = kernel_source_hash()
+    traffic = None
+    mt = MEASURED_TRAFFIC.get(args.workload)
+    if mt and mt.get("kernel_hash") == src_hash:
+        traffic = mt["bytes_per_launch"]
+    roofline = {
+        "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+        "frac": round(achieved / peak, 4), "traffic": traffic,
+        "kernel": kernels[0] if len(kernels) == 1 else kernels,
+        "avg_launch_us": [round(float(x) * 1e3, 2) for x in avg_ms],
+        "algorithmic_flops_per_launch": [int(x) for x in flops_launch],
+        "algorithmic_bytes_per_launch": [int(x) for x in bytes_launch],
+    }
+
+    value = flops_step / (ms_step * 1e-3) / 1e9
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+    vs = None
+    if all(n in PAGE_MS for n in names):
+        page_gflops = flops_step / (sum(PAGE_MS[n] for n in names) * 1e-3) / 1e9
+        vs = round(value / page_gflops, 2)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(insts, sets, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs,
+        "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "launches": [{"name": i.name, "a_type": synth.TYPE_NAMES[i.a_type],
+                          "ne00": i.ne[0], "K": i.ne[1], "ne10": i.ne[4],
+                          "slices": i.ne[10] * i.ne[11]} for i in insts],
+            "rotating_input_sets": R,
+        },
+        "gbps": round(gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    if vs is not None:
+        out["vs_baseline_note"] = ("ratio to the pages' float-staging per-op times for the same "
+                                   "shapes on an Apple M5 (Metal): another machine, context only")
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(insts, sets, target_s):
+    """Time the CPU oracle, as it stands, on a bounded sample of the same
+    workload: all ne00 outputs of a few dst columns of every launch.  The
+    sample grows until it takes about target_s seconds.  The same columns of
+    the GPU result are checked against it (max error ratio reported)."""
+    import oracle
+    import torch
+
+    threads = oracle.num_threads()
+    rng = np.random.default_rng(123)
+    n = max(1, threads // 2)
+    total_flops, total_t, sample_desc, worst = 0, 0.0, [], 0.0
+    while True:
+        t_all, f_all = 0.0, 0
+        results = []
+        for j, inst in enumerate(insts):
+            ne = inst.ne
+            slices = ne[10] * ne[11]
+            cnt = min(n, ne[4] * slices)
+            flat = rng.choice(ne[4] * slices, cnt, replace=False)
+            cols = np.array([[c % ne[4], (c // ne[4]) % ne[10], c // (ne[4] * ne[10])] for c in flat])
+            t = time.perf_counter()
+            ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, ne, inst.nb, cols=cols)
+            t_all += time.perf_counter() - t
+            f_all += 2 * ne[0] * ne[1] * cnt
+            results.append((j, cols, ref, den))
+        log("cpu oracle sample: %d columns/launch, %.2f s" % (n, t_all))
+        if t_all >= 0.4 * target_s or n >= 4096:
+            break
+        n = int(n * min(8.0, max(1.5, target_s / max(t_all, 1e-3))))
+    total_flops, total_t = f_all, t_all
+    for j, cols, ref, den in results:
+        d = sets[0][j][2].cpu().numpy()
+        g = np.stack([d[i3, i2, i1] for i1, i2, i3 in cols])
+        worst = max(worst, oracle.check(g, ref, den)["max_ratio"])
+        sample_desc.append("%s: %d dst columns x %d" % (insts[j].name, len(cols), insts[j].ne[0]))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        cpu_model = platform.processor()
+    return {
+        "value": round(total_flops / total_t / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": "; ".join(sample_desc) + " (double accumulation, %.1f s)" % total_t,
+        "cpu_model": cpu_model,
+        "sample_parity_max_ratio": worst,
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * outprod.h -- C ABI of liboutprod.so: ggml's OUT_PROD on an MI355X (gfx950).
+ *
+ * The operation (pages: "metal: OUT_PROD runs batched, broadcast and narrow
+ * shapes on the GPU", body and review "VERIFIED BY READING"; "metal: OUT_PROD
+ * multiplies in float staging", body):
+ *
+ *   dst[i0,i1,i2,i3] = sum_{k<K} a[i0,k,i2/dps2,i3/dps3] * b[i1,k,i2,i3]
+ *   dps2 = ne12/ne02,  dps3 = ne13/ne03          (integer division)
+ *
+ * It is the whole matmul backward of a training graph: the gradient of a
+ * weight is out_prod(activation, grad) and the gradient of an input is
+ * out_prod(weight, grad^T).  dst has the shape {a.ne0, b.ne0, b.ne2, b.ne3};
+ * a's slice dims must divide b's (grouped-head broadcast: consecutive dst
+ * slices share one a slice).  a may be f32 of any width, or a frozen
+ * quantized weight (q8_0, q4_K) that is dequantized to f32 in registers.
+ * b and dst are f32.  Every value is staged and accumulated in fp32; nothing
+ * passes through half precision (training gradients exceed half's 65504).
+ *
+ * Tensor description (ggml convention, dim 0 fastest):
+ *   ne[12] = { a.ne[0..3], b.ne[0..3], dst.ne[0..3] }   element counts
+ *            a = [ne00, K, ne02, ne03], b = [ne10, K, ne12, ne13],
+ *            dst = [ne00, ne10, ne12, ne13]
+ *   nb[12] = byte strides in the same order.
+ *     nb[0]: 4 for f32 a, else the block size in bytes (34 for q8_0, 144 for
+ *            q4_K); nb[4] and nb[8] must be 4 (dim 0 is contiguous).
+ *     nb[1..3], nb[5..7], nb[9..11]: any non-negative byte strides (views,
+ *            padded rows, stride-0 broadcast of inputs), aligned to 4 bytes
+ *            (2 for q8_0 a).  dst's dims must not overlap one another.
+ *
+ * Memory and ownership: a, b and dst are DEVICE pointers owned by the caller.
+ * The library keeps no pointer after a call returns, allocates nothing and
+ * holds no mutable state, so calls may come from any thread.  A call only
+ * enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
+ * returns; the buffers must stay alive until the stream has passed it.
+ * dst is overwritten (not accumulated into).  Results are deterministic:
+ * every dst element has one writer and a fixed summation order.
+ *
+ * Errors: every function returns OUTPROD_OK (0) or a negative status.  All
+ * argument checks happen on the host before any HIP call, and on error dst
+ * is left untouched.  Checks run in this order: NULL ne/nb, a_type,
+ * negative extents, K mismatch, dst shape, (empty dst: success, no work),
+ * broadcast divisibility, quant block width, strides/alignment, NULL data
+ * pointers, index range, aliasing, kernel override.
+ */
+#ifndef OUTPROD_H
+#define OUTPROD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* a_type: the GGUF tensor type ids. */
+#define OUTPROD_TYPE_F32 0
+#define OUTPROD_TYPE_Q8_0 8  /* 34-byte block: fp16 d, int8 q[32]; value = d*q */
+#define OUTPROD_TYPE_Q4_K 12 /* 144-byte block of 256: fp16 d, fp16 dmin, 12 bytes of
+                                6-bit (scale, min) for 8 sub-blocks of 32, 128 bytes
+                                of 4-bit q; value = d*scale*q - dmin*min */
+
+/* status codes */
+#define OUTPROD_OK 0
+#define OUTPROD_E_NULL (-1)      /* ne/nb NULL, or a data pointer NULL where data is read/written */
+#define OUTPROD_E_TYPE (-2)      /* a_type is not F32, Q8_0 or Q4_K */
+#define OUTPROD_E_SHAPE (-3)     /* a negative extent */
+#define OUTPROD_E_K (-4)         /* a.ne[1] != b.ne[1] */
+#define OUTPROD_E_DST_SHAPE (-5) /* dst.ne != {a.ne0, b.ne0, b.ne2, b.ne3} */
+#define OUTPROD_E_BCAST (-6)     /* b.ne2 % a.ne2 or b.ne3 % a.ne3 != 0 (or a.ne2/a.ne3 < 1) */
+#define OUTPROD_E_QK (-7)        /* quantized a whose width is not a whole number of blocks */
+#define OUTPROD_E_LAYOUT (-8)    /* bad nb[0], negative or misaligned stride or pointer,
+                                    overlapping dst dims */
+#define OUTPROD_E_ALIAS (-9)     /* dst's bytes overlap a's or b's */
+#define OUTPROD_E_RANGE (-10)    /* an extent overflows the kernels' index range */
+#define OUTPROD_E_KERNEL (-11)   /* a forced kernel that cannot run this problem */
+#define OUTPROD_E_HIP (-12)      /* the kernel launch failed (e.g. no gfx950 device) */
+
+/*
+ * out_prod: dst = OUT_PROD(a, b) as defined above, enqueued on `stream`.
+ * a: device pointer to a's first byte (f32 values or packed blocks).
+ * b: device pointer to b's first float.  dst: device pointer to dst's first
+ * float.  ne/nb: host arrays of 12 int64 each (read during the call only).
+ * K == 0 writes zeros; an empty dst returns OUTPROD_OK without launching.
+ */
+int out_prod(const void *a, int a_type, const float *b, float *dst,
+             const int64_t ne[12], const int64_t nb[12], void *stream);
+
+/* Kernel families (for out_prod_plan's report and out_prod_ex's override). */
+#define OUTPROD_KERNEL_AUTO 0   /* let the library choose */
+#define OUTPROD_KERNEL_SKINNY 1 /* f32 a, ne00 <= 32: bandwidth-bound MFMA 16x16x4 column
+                                   kernel, K split over the waves of a workgroup */
+#define OUTPROD_KERNEL_TILED 2  /* LDS-staged fp32 tiles, MFMA 32x32x2, any a type/shape */
+#define OUTPROD_KERNEL_ZERO 3   /* K == 0: writes zeros */
+#define OUTPROD_KERNEL_NONE 4   /* empty dst: nothing to do */
+
+/* What a call would launch.  Filled by out_prod_plan (host only). */
+typedef struct outprod_plan {
+    int kernel;       /* OUTPROD_KERNEL_* */
+    int tile_m;       /* dst tile along i0 (ne00) */
+    int tile_n;       /* dst tile along i1 (ne10) */
+    int tile_k;       /* K rows per pipeline stage (tiled) or per wave step (skinny) */
+    int block;        /* threads per workgroup */
+    int lds_bytes;    /* static LDS per workgroup */
+    int64_t grid;     /* workgroups in the single launch */
+    int64_t slices;   /* ne12 * ne13 */
+    int64_t dps2;     /* ne12 / ne02 */
+    int64_t dps3;     /* ne13 / ne03 */
+    int64_t flops;    /* 2 * ne00 * ne10 * K * slices */
+} outprod_plan;
+
+/*
+ * out_prod_plan: run every check of out_prod and describe the launch it
+ * would make with `kernel` (OUTPROD_KERNEL_AUTO for the library's choice),
+ * without touching the device or any HIP API.  The data pointers are only
+ * checked (NULL, alignment, aliasing), never dereferenced.  plan must be
+ * non-NULL (else OUTPROD_E_NULL).
+ */
+int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
+                  const int64_t ne[12], const int64_t nb[12], int kernel,
+                  outprod_plan *plan);
+
+/*
+ * out_prod_ex: out_prod with the kernel family forced (OUTPROD_KERNEL_AUTO,
+ * _SKINNY or _TILED), for A/B measurements and for testing both kernels on
+ * the same problem.  A family that cannot run the problem returns
+ * OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a or ne00 > 32).
+ */
+int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
+                const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);
+
+/* A static English description of a status code; never NULL. */
+const char *out_prod_strerror(int status);
+
+/* Library ABI version: 1. */
+int out_prod_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OUTPROD_H */

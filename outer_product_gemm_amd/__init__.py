@@ -18,6 +18,6 @@ __all__ = ["F32", "Q8_0", "Q4_K", "binding"]
 
 def __getattr__(name):
     if name == "binding":
-        from . import binding
-        return binding
+        import importlib
+        return importlib.import_module(__name__ + ".binding")
     raise AttributeError(name)

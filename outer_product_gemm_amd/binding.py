@@ -1,0 +1,188 @@
+"""Python binding of liboutprod.so: argument marshalling only.
+
+The names follow the C ABI in ``include/outprod.h``:
+
+* :func:`out_prod` / :func:`out_prod_ex` take raw device addresses (ints), the
+  ``ne``/``nb`` arrays and a ``hipStream_t`` address, exactly like the C calls;
+* :func:`out_prod_plan` runs the host-side checks and reports the launch;
+* :func:`out_prod_strerror` / :func:`out_prod_version`.
+
+:func:`out_prod_tensors` is a convenience that reads ``ne``/``nb`` off torch
+tensors and uses torch's current stream.  Every step of the computation runs
+in the library's HIP kernels; if the library is missing, the first call raises.
+
+torch is imported before the library is loaded: torch ships its own
+``libamdhip64.so.7``, and loading it first makes the library bind to the same
+HIP runtime (same SONAME), so torch's device pointers and streams are valid in
+both.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # noqa: F401  (must precede loading the library; see above)
+
+F32, Q8_0, Q4_K = 0, 8, 12
+BLOCK_VALUES = {F32: 1, Q8_0: 32, Q4_K: 256}
+BLOCK_BYTES = {F32: 4, Q8_0: 34, Q4_K: 144}
+
+OUTPROD_OK = 0
+STATUS = {
+    -1: "E_NULL", -2: "E_TYPE", -3: "E_SHAPE", -4: "E_K", -5: "E_DST_SHAPE", -6: "E_BCAST",
+    -7: "E_QK", -8: "E_LAYOUT", -9: "E_ALIAS", -10: "E_RANGE", -11: "E_KERNEL", -12: "E_HIP",
+}
+KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
+KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
+
+# Every symbol the header declares.
+EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_strerror", "out_prod_version")
+
+
+class OutProdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("out_prod failed: %s (%d): %s" % (STATUS.get(status, "?"), status, message))
+        self.status = status
+
+
+class outprod_plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
+                ("tile_k", ctypes.c_int), ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
+                ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64)]
+
+
+_I64x12 = ctypes.c_int64 * 12
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liboutprod.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("liboutprod.so is not built (%s); run __graft_entry__.build() "
+                                   "or python -m outer_product_gemm_amd.build" % path)
+            lib = ctypes.CDLL(path)
+            vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+            lib.out_prod.argtypes = [vp, ctypes.c_int, vp, vp, i64p, i64p, vp]
+            lib.out_prod.restype = ctypes.c_int
+            lib.out_prod_ex.argtypes = [vp, ctypes.c_int, vp, vp, i64p, i64p, vp, ctypes.c_int]
+            lib.out_prod_ex.restype = ctypes.c_int
+            lib.out_prod_plan.argtypes = [vp, ctypes.c_int, vp, vp, i64p, i64p, ctypes.c_int,
+                                          ctypes.POINTER(outprod_plan)]
+            lib.out_prod_plan.restype = ctypes.c_int
+            lib.out_prod_strerror.argtypes = [ctypes.c_int]
+            lib.out_prod_strerror.restype = ctypes.c_char_p
+            lib.out_prod_version.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _arr12(x):
+    vals = [int(v) for v in x]
+    if len(vals) != 12:
+        raise ValueError("ne/nb must have 12 entries")
+    return _I64x12(*vals)
+
+
+def _check(status: int) -> None:
+    if status != OUTPROD_OK:
+        raise OutProdError(status, out_prod_strerror(status))
+
+
+def out_prod_strerror(status: int) -> str:
+    return load_library().out_prod_strerror(int(status)).decode()
+
+
+def out_prod_version() -> int:
+    return int(load_library().out_prod_version())
+
+
+def out_prod(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0) -> None:
+    """C ``out_prod`` on raw device addresses.  Raises OutProdError on a nonzero status."""
+    _check(load_library().out_prod(a or None, int(a_type), b or None, dst or None,
+                                   _arr12(ne), _arr12(nb), stream or None))
+
+
+def out_prod_ex(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0,
+                kernel: int = KERNEL_AUTO) -> None:
+    """C ``out_prod_ex``: out_prod with the kernel family forced."""
+    _check(load_library().out_prod_ex(a or None, int(a_type), b or None, dst or None,
+                                      _arr12(ne), _arr12(nb), stream or None, int(kernel)))
+
+
+def out_prod_status(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0,
+                    kernel: int = KERNEL_AUTO) -> int:
+    """``out_prod_ex`` returning the raw status instead of raising."""
+    return int(load_library().out_prod_ex(a or None, int(a_type), b or None, dst or None,
+                                          _arr12(ne), _arr12(nb), stream or None, int(kernel)))
+
+
+def out_prod_plan(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = KERNEL_AUTO) -> dict:
+    """C ``out_prod_plan``: host-side checks and the launch a call would make."""
+    p = outprod_plan()
+    _check(load_library().out_prod_plan(a or None, int(a_type), b or None, dst or None,
+                                        _arr12(ne), _arr12(nb), int(kernel), ctypes.byref(p)))
+    d = {name: getattr(p, name) for name, _ in outprod_plan._fields_}
+    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
+    return d
+
+
+def plan_status(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = KERNEL_AUTO) -> int:
+    """``out_prod_plan`` returning the raw status instead of raising."""
+    p = outprod_plan()
+    return int(load_library().out_prod_plan(a or None, int(a_type), b or None, dst or None,
+                                            _arr12(ne), _arr12(nb), int(kernel), ctypes.byref(p)))
+
+
+# ---------------------------------------------------------------- torch tensors
+
+def tensor_ne_nb(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tensor, a_ne0=None):
+    """ggml ne/nb of torch tensors laid out (ne3, ne2, ne1, ne0) (fewer dims are
+    padded with leading 1s).  A quantized ``a`` is a uint8 tensor whose last dim
+    is the row's bytes; ``a_ne0`` gives its value count."""
+    def four(t):
+        shape = [1] * (4 - t.dim()) + list(t.shape)
+        stride = [0] * (4 - t.dim()) + list(t.stride())
+        return shape[::-1], stride[::-1]
+    ash, ast = four(a)
+    bsh, bst = four(b)
+    osh, ost = four(out)
+    if a_type == F32:
+        a_ne = ash
+        a_nb = [4 * s for s in ast]
+    else:
+        if a_ne0 is None:
+            a_ne0 = ash[0] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]
+        a_ne = [a_ne0] + ash[1:]
+        a_nb = [BLOCK_BYTES[a_type]] + list(ast[1:])
+    ne = a_ne + bsh + osh
+    nb = a_nb + [4 * s for s in bst] + [4 * s for s in ost]
+    return ne, nb
+
+
+def out_prod_tensors(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tensor = None,
+                     a_ne0: int = None, kernel: int = KERNEL_AUTO, stream=None) -> torch.Tensor:
+    """OUT_PROD of torch device tensors on the current (or given) stream.
+
+    a: f32 (ne03, ne02, K, ne00), or uint8 (ne03, ne02, K, row_bytes) for q8_0/q4_K;
+    b: f32 (ne13, ne12, K, ne10); out: f32 (ne13, ne12, ne10, ne00), allocated if None.
+    """
+    if out is None:
+        bsh = [1] * (4 - b.dim()) + list(b.shape)
+        if a_type == F32:
+            ne00 = a.shape[-1]
+        else:
+            ne00 = a_ne0 if a_ne0 is not None else a.shape[-1] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]
+        out = torch.empty((bsh[0], bsh[1], bsh[3], ne00), dtype=torch.float32, device=b.device)
+    ne, nb = tensor_ne_nb(a, a_type, b, out, a_ne0)
+    if stream is None:
+        stream = torch.cuda.current_stream(b.device)
+    out_prod_ex(a.data_ptr(), a_type, b.data_ptr(), out.data_ptr(), ne, nb, stream.cuda_stream, kernel)
+    return out

@@ -1,0 +1,263 @@
+// api.cpp -- the C entry points of liboutprod.so: host-side validation of the
+// OUT_PROD contract, kernel planning and the single launch.
+//
+// The contract (pages: "metal: OUT_PROD runs batched, broadcast and narrow
+// shapes on the GPU", review "VERIFIED BY READING"): dst is {a.ne0, b.ne0,
+// b.ne2, b.ne3}; b.ne2 % a.ne2 == 0 and b.ne3 % a.ne3 == 0; slice i2 of dst
+// reads a slice i2/dps2.  The same page's body scopes the width rule to the
+// quantized copy only, so an f32 a of any width is accepted and a quantized a
+// needs only whole blocks.  Unsupported problems are refused with a status
+// code before any HIP call; there is no silent fallback.
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "outprod.h"
+#include "outprod_internal.h"
+
+namespace outprod {
+namespace {
+
+int block_values(int t) { return t == OUTPROD_TYPE_Q8_0 ? 32 : t == OUTPROD_TYPE_Q4_K ? 256 : 1; }
+int block_bytes(int t) { return t == OUTPROD_TYPE_Q8_0 ? 34 : t == OUTPROD_TYPE_Q4_K ? 144 : 4; }
+int align_of(int t) { return t == OUTPROD_TYPE_Q8_0 ? 2 : 4; }
+
+// x*y + z for non-negative int64, false on overflow.
+bool mul_add(int64_t x, int64_t y, int64_t z, int64_t *out) {
+    __int128 r = (__int128)x * y + z;
+    if (r > INT64_MAX) return false;
+    *out = (int64_t)r;
+    return true;
+}
+
+// Bytes spanned by a 4-d view: last byte offset + 1.  dim0_bytes is the byte
+// length of one row along dim 0.  False on overflow.
+bool extent(int64_t dim0_bytes, const int64_t *ne, const int64_t *nb, int64_t *out) {
+    int64_t e = dim0_bytes;
+    for (int d = 1; d < 4; ++d)
+        if (ne[d] > 1 && !mul_add(ne[d] - 1, nb[d], e, &e)) return false;
+    *out = e;
+    return true;
+}
+
+bool overlaps(const void *p, int64_t np, const void *q, int64_t nq) {
+    if (np <= 0 || nq <= 0) return false;
+    uintptr_t a0 = (uintptr_t)p, a1 = a0 + (uintptr_t)np;
+    uintptr_t b0 = (uintptr_t)q, b1 = b0 + (uintptr_t)nq;
+    return a0 < b1 && b0 < a1;
+}
+
+struct Checked {
+    Problem p;
+    Launch l;
+};
+
+int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
+                      const int64_t *ne, const int64_t *nb, int kernel, Checked *c) {
+    if (!ne || !nb) return OUTPROD_E_NULL;
+    if (a_type != OUTPROD_TYPE_F32 && a_type != OUTPROD_TYPE_Q8_0 && a_type != OUTPROD_TYPE_Q4_K)
+        return OUTPROD_E_TYPE;
+    for (int i = 0; i < 12; ++i)
+        if (ne[i] < 0) return OUTPROD_E_SHAPE;
+    const int64_t ne00 = ne[0], K = ne[1], ne02 = ne[2], ne03 = ne[3];
+    const int64_t ne10 = ne[4], ne12 = ne[6], ne13 = ne[7];
+    if (ne[5] != K) return OUTPROD_E_K;
+    if (ne[8] != ne00 || ne[9] != ne10 || ne[10] != ne12 || ne[11] != ne13)
+        return OUTPROD_E_DST_SHAPE;
+
+    memset(c, 0, sizeof(*c));
+    Problem &p = c->p;
+    Launch &l = c->l;
+    p.a_type = a_type;
+    p.M = ne00;
+    p.N = ne10;
+    p.K = K;
+    p.ne12 = ne12;
+    p.ne13 = ne13;
+
+    const bool empty = ne00 == 0 || ne10 == 0 || ne12 == 0 || ne13 == 0;
+    if (empty) {
+        if (kernel != OUTPROD_KERNEL_AUTO && kernel != OUTPROD_KERNEL_SKINNY &&
+            kernel != OUTPROD_KERNEL_TILED)
+            return OUTPROD_E_KERNEL;
+        l.kernel = OUTPROD_KERNEL_NONE;
+        return OUTPROD_OK;
+    }
+
+    if (ne02 < 1 || ne03 < 1 || ne12 % ne02 != 0 || ne13 % ne03 != 0) return OUTPROD_E_BCAST;
+    p.dps2 = ne12 / ne02;
+    p.dps3 = ne13 / ne03;
+
+    if (ne00 % block_values(a_type) != 0) return OUTPROD_E_QK;
+
+    // strides and alignment
+    if (nb[0] != block_bytes(a_type) || nb[4] != 4 || nb[8] != 4) return OUTPROD_E_LAYOUT;
+    for (int i = 0; i < 12; ++i)
+        if (nb[i] < 0) return OUTPROD_E_LAYOUT;
+    const int al = align_of(a_type);
+    for (int i = 1; i < 4; ++i)
+        if (nb[i] % al != 0 || nb[4 + i] % 4 != 0 || nb[8 + i] % 4 != 0) return OUTPROD_E_LAYOUT;
+    if ((uintptr_t)a % al != 0 || (uintptr_t)b % 4 != 0 || (uintptr_t)dst % 4 != 0)
+        return OUTPROD_E_LAYOUT;
+    // dst dims must be ordered and disjoint so that every element has one address
+    {
+        int64_t span = 4 * ne00;  // bytes of one dst row
+        for (int d = 1; d < 4; ++d) {
+            if (ne[8 + d] > 1) {
+                if (nb[8 + d] < span) return OUTPROD_E_LAYOUT;
+                if (!mul_add(ne[8 + d] - 1, nb[8 + d], span, &span)) return OUTPROD_E_RANGE;
+            }
+        }
+    }
+
+    if (!dst) return OUTPROD_E_NULL;
+    if (K > 0 && (!a || !b)) return OUTPROD_E_NULL;
+
+    // index range: the kernels index workgroups, rows and columns with 32-bit ints
+    const int64_t lim = INT32_MAX;
+    int64_t slices;
+    if (!mul_add(ne12, ne13, 0, &slices) || slices > lim || ne00 > lim || ne10 > lim || K > lim)
+        return OUTPROD_E_RANGE;
+    const int64_t a_row = ne00 / block_values(a_type) * block_bytes(a_type);
+    int64_t ext_a = 0, ext_b = 0, ext_d = 0;
+    if (K > 0) {
+        const int64_t ane[4] = {ne00, K, ne02, ne03}, anb[4] = {nb[0], nb[1], nb[2], nb[3]};
+        const int64_t bne[4] = {ne10, K, ne12, ne13}, bnb[4] = {4, nb[5], nb[6], nb[7]};
+        if (!extent(a_row, ane, anb, &ext_a) || !extent(4 * ne10, bne, bnb, &ext_b))
+            return OUTPROD_E_RANGE;
+    }
+    {
+        const int64_t dne[4] = {ne00, ne10, ne12, ne13}, dnb[4] = {4, nb[9], nb[10], nb[11]};
+        if (!extent(4 * ne00, dne, dnb, &ext_d)) return OUTPROD_E_RANGE;
+    }
+    if (K > 0 && (overlaps(dst, ext_d, a, ext_a) || overlaps(dst, ext_d, b, ext_b)))
+        return OUTPROD_E_ALIAS;
+
+    p.a = (const uint8_t *)a;
+    p.b = (const uint8_t *)b;
+    p.dst = (uint8_t *)dst;
+    p.nb01 = nb[1];
+    p.nb02 = nb[2];
+    p.nb03 = nb[3];
+    p.nb11 = nb[5];
+    p.nb12 = nb[6];
+    p.nb13 = nb[7];
+    p.nb1 = nb[9];
+    p.nb2 = nb[10];
+    p.nb3 = nb[11];
+    p.vec_a = a_type == OUTPROD_TYPE_F32 && (uintptr_t)a % 16 == 0 && nb[1] % 16 == 0 &&
+              nb[2] % 16 == 0 && nb[3] % 16 == 0;
+    p.vec_b = (uintptr_t)b % 16 == 0 && nb[5] % 16 == 0 && nb[6] % 16 == 0 && nb[7] % 16 == 0;
+
+    if (K == 0) {
+        if (kernel != OUTPROD_KERNEL_AUTO && kernel != OUTPROD_KERNEL_SKINNY &&
+            kernel != OUTPROD_KERNEL_TILED)
+            return OUTPROD_E_KERNEL;
+        plan_zero(p, &l);
+        return l.grid > lim ? OUTPROD_E_RANGE : OUTPROD_OK;
+    }
+
+    bool ok;
+    switch (kernel) {
+    case OUTPROD_KERNEL_AUTO:
+        ok = plan_skinny(p, &l) || plan_tiled(p, &l);
+        break;
+    case OUTPROD_KERNEL_SKINNY:
+        ok = plan_skinny(p, &l);
+        break;
+    case OUTPROD_KERNEL_TILED:
+        ok = plan_tiled(p, &l);
+        break;
+    default:
+        ok = false;
+    }
+    if (!ok) return OUTPROD_E_KERNEL;
+    if (l.grid > lim) return OUTPROD_E_RANGE;
+    return OUTPROD_OK;
+}
+
+int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne,
+        const int64_t *nb, void *stream, int kernel) {
+    Checked c;
+    int rc = validate_and_plan(a, a_type, b, dst, ne, nb, kernel, &c);
+    if (rc != OUTPROD_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    switch (c.l.kernel) {
+    case OUTPROD_KERNEL_NONE:
+        return OUTPROD_OK;
+    case OUTPROD_KERNEL_ZERO:
+        e = launch_zero(c.p, c.l, s);
+        break;
+    case OUTPROD_KERNEL_SKINNY:
+        e = launch_skinny(c.p, c.l, s);
+        break;
+    case OUTPROD_KERNEL_TILED:
+        e = launch_tiled(c.p, c.l, s);
+        break;
+    default:
+        return OUTPROD_E_KERNEL;
+    }
+    return e == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
+}
+
+}  // namespace
+}  // namespace outprod
+
+extern "C" {
+
+int out_prod(const void *a, int a_type, const float *b, float *dst, const int64_t ne[12],
+             const int64_t nb[12], void *stream) {
+    return outprod::run(a, a_type, b, dst, ne, nb, stream, OUTPROD_KERNEL_AUTO);
+}
+
+int out_prod_ex(const void *a, int a_type, const float *b, float *dst, const int64_t ne[12],
+                const int64_t nb[12], void *stream, int kernel) {
+    return outprod::run(a, a_type, b, dst, ne, nb, stream, kernel);
+}
+
+int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
+                  const int64_t ne[12], const int64_t nb[12], int kernel, outprod_plan *plan) {
+    if (!plan) return OUTPROD_E_NULL;
+    outprod::Checked c;
+    int rc = outprod::validate_and_plan(a, a_type, b, dst, ne, nb, kernel, &c);
+    if (rc != OUTPROD_OK) return rc;
+    memset(plan, 0, sizeof(*plan));
+    plan->kernel = c.l.kernel;
+    plan->tile_m = c.l.tile_m;
+    plan->tile_n = c.l.tile_n;
+    plan->tile_k = c.l.tile_k;
+    plan->block = c.l.block;
+    plan->lds_bytes = c.l.lds_bytes;
+    plan->grid = c.l.grid;
+    plan->slices = c.p.ne12 * c.p.ne13;
+    plan->dps2 = c.p.dps2;
+    plan->dps3 = c.p.dps3;
+    plan->flops = 2 * c.p.M * c.p.N * c.p.K * plan->slices;
+    return OUTPROD_OK;
+}
+
+const char *out_prod_strerror(int status) {
+    switch (status) {
+    case OUTPROD_OK: return "success";
+    case OUTPROD_E_NULL: return "NULL pointer where memory is required";
+    case OUTPROD_E_TYPE: return "unsupported a_type (expected F32, Q8_0 or Q4_K)";
+    case OUTPROD_E_SHAPE: return "negative extent";
+    case OUTPROD_E_K: return "a.ne[1] != b.ne[1] (contraction length mismatch)";
+    case OUTPROD_E_DST_SHAPE: return "dst shape is not {a.ne0, b.ne0, b.ne2, b.ne3}";
+    case OUTPROD_E_BCAST: return "b.ne2/b.ne3 not divisible by a.ne2/a.ne3";
+    case OUTPROD_E_QK: return "quantized a width is not a whole number of blocks";
+    case OUTPROD_E_LAYOUT: return "unsupported strides, alignment or overlapping dst dims";
+    case OUTPROD_E_ALIAS: return "dst overlaps an input";
+    case OUTPROD_E_RANGE: return "extent exceeds the supported index range";
+    case OUTPROD_E_KERNEL: return "the requested kernel cannot run this problem";
+    case OUTPROD_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int out_prod_version(void) { return 1; }
+
+}  // extern "C"

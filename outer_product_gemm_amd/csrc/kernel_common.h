@@ -1,0 +1,60 @@
+// kernel_common.h -- device-side helpers shared by the OUT_PROD kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "outprod_internal.h"
+
+namespace outprod {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Workgroup -> logical tile remap so that consecutive logical tiles run on the
+// same XCD.  The MI355X's 8 XCDs each have their own L2 and the dispatcher
+// deals workgroups to them round-robin; neighbouring tiles share cache lines
+// (skinny kernel) or operand panels (tiled kernel).  Bijective for any grid.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+    const int nx = 8;
+    const int xcd = bid % nx, local = bid / nx;
+    const int per = grid / nx, rem = grid % nx;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// IEEE binary16 bits -> float, exactly, by bit manipulation (normal numbers
+// are rebiased, subnormals are f * 2^-24, Inf/NaN keep their class).
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    const uint32_t sign = (h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu;
+    const uint32_t f = h & 0x3FFu;
+    if (e == 0) {
+        const float v = (float)f * 0x1p-24f;  // f < 2^10: exact
+        return __uint_as_float(__float_as_uint(v) | sign);
+    }
+    const uint32_t ee = e == 31 ? 0xFFu : e + 112u;
+    return __uint_as_float(sign | (ee << 23) | (f << 13));
+}
+
+// Grouped-head broadcast: dst slice z = i2 + ne12*i3 reads a slice
+// (i2/dps2, i3/dps3) and b slice (i2, i3).
+struct SliceBase {
+    const uint8_t *a;
+    const uint8_t *b;
+    uint8_t *dst;
+};
+
+__device__ __forceinline__ SliceBase slice_base(const Problem &p, int z) {
+    const int64_t i2 = z % p.ne12, i3 = z / p.ne12;
+    const int64_t i02 = i2 / p.dps2, i03 = i3 / p.dps3;
+    SliceBase s;
+    s.a = p.a + i02 * p.nb02 + i03 * p.nb03;
+    s.b = p.b + i2 * p.nb12 + i3 * p.nb13;
+    s.dst = p.dst + i2 * p.nb2 + i3 * p.nb3;
+    return s;
+}
+
+__device__ __forceinline__ float ldf(const uint8_t *p) { return *(const float *)p; }
+
+}  // namespace outprod

@@ -1,0 +1,154 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and refuses every contract violation with its status code before any HIP call
+(so these run without a GPU).  Data pointers here are fake addresses that are
+never dereferenced: out_prod_plan only checks them, and out_prod returns on
+the failed check before touching the device."""
+import os
+import re
+
+import pytest
+
+from outer_product_gemm_amd import binding as B
+from outer_product_gemm_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A, BB, D = 0x10000000, 0x20000000, 0x30000000   # fake, 256-aligned, disjoint
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "outprod.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    lib = B.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    assert B.out_prod_version() == 1
+    for code in [0] + list(B.STATUS):
+        msg = B.out_prod_strerror(code)
+        assert msg and msg != "unknown status"
+    assert B.out_prod_strerror(-999) == "unknown status"
+
+
+def base(a_type=synth.F32, a_ne=(8, 512, 1, 1), b_ne=(2560, 512, 1, 1)):
+    ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
+    return list(ne), list(nb)
+
+
+def plan(a_type, ne, nb, a=A, b=BB, d=D, kernel=0):
+    return B.plan_status(a, a_type, b, d, ne, nb, kernel)
+
+
+def test_valid_problem_plans():
+    ne, nb = base()
+    assert plan(synth.F32, ne, nb) == 0
+    p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb)
+    assert p["kernel_name"] == "skinny" and p["slices"] == 1 and p["flops"] == 2 * 8 * 2560 * 512
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda ne, nb: ne.__setitem__(5, 511), "E_K"),
+    (lambda ne, nb: ne.__setitem__(8, 9), "E_DST_SHAPE"),
+    (lambda ne, nb: ne.__setitem__(9, 2561), "E_DST_SHAPE"),
+    (lambda ne, nb: ne.__setitem__(0, -1), "E_SHAPE"),
+    (lambda ne, nb: nb.__setitem__(0, 8), "E_LAYOUT"),      # a not unit stride
+    (lambda ne, nb: nb.__setitem__(4, 2048), "E_LAYOUT"),   # transposed b view
+    (lambda ne, nb: nb.__setitem__(8, 8), "E_LAYOUT"),
+    (lambda ne, nb: nb.__setitem__(5, 10242), "E_LAYOUT"),  # misaligned stride
+    (lambda ne, nb: nb.__setitem__(9, 16), "E_LAYOUT"),     # dst rows overlap
+    (lambda ne, nb: nb.__setitem__(1, -32), "E_LAYOUT"),
+])
+def test_contract_violations(mutate, code):
+    ne, nb = base()
+    mutate(ne, nb)
+    assert B.STATUS[plan(synth.F32, ne, nb)] == code
+    # out_prod itself returns the same status without touching the device
+    assert B.STATUS[B.out_prod_status(A, synth.F32, BB, D, ne, nb)] == code
+
+
+def test_broadcast_divisibility():
+    ne, nb = base(a_ne=(128, 512, 4, 1), b_ne=(128, 512, 16, 1))
+    assert plan(synth.F32, ne, nb) == 0
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["dps2"] == 4
+    ne, nb = base(a_ne=(128, 512, 3, 1), b_ne=(128, 512, 16, 1))
+    assert B.STATUS[plan(synth.F32, ne, nb)] == "E_BCAST"
+    ne, nb = base(a_ne=(128, 512, 1, 2), b_ne=(128, 512, 1, 3))
+    assert B.STATUS[plan(synth.F32, ne, nb)] == "E_BCAST"
+
+
+def test_type_and_block_width():
+    ne, nb = base()
+    assert B.STATUS[plan(1, ne, nb)] == "E_TYPE"
+    assert B.STATUS[plan(99, ne, nb)] == "E_TYPE"
+    ne, nb = base(synth.Q8_0, a_ne=(64, 512, 1, 1))
+    assert plan(synth.Q8_0, ne, nb) == 0
+    ne[0] = ne[8] = 48
+    assert B.STATUS[plan(synth.Q8_0, ne, nb)] == "E_QK"
+    ne, nb = base(synth.Q4_K, a_ne=(512, 64, 1, 1), b_ne=(16, 64, 1, 1))
+    assert plan(synth.Q4_K, ne, nb) == 0
+    ne[0] = ne[8] = 384
+    assert B.STATUS[plan(synth.Q4_K, ne, nb)] == "E_QK"
+    # quant blocks must be addressed with their byte size as nb[0]
+    ne, nb = base(synth.Q4_K, a_ne=(512, 64, 1, 1), b_ne=(16, 64, 1, 1))
+    nb[0] = 4
+    assert B.STATUS[plan(synth.Q4_K, ne, nb)] == "E_LAYOUT"
+
+
+def test_pointer_checks():
+    ne, nb = base()
+    assert B.STATUS[plan(synth.F32, ne, nb, a=0)] == "E_NULL"
+    assert B.STATUS[plan(synth.F32, ne, nb, b=0)] == "E_NULL"
+    assert B.STATUS[plan(synth.F32, ne, nb, d=0)] == "E_NULL"
+    assert B.STATUS[plan(synth.F32, ne, nb, b=BB + 2)] == "E_LAYOUT"
+    assert B.STATUS[plan(synth.F32, ne, nb, d=BB + 4096)] == "E_ALIAS"   # dst inside b
+    assert B.STATUS[plan(synth.F32, ne, nb, d=A + 4)] == "E_ALIAS"
+    # q8_0 rows are 2-byte aligned: an odd address is refused, an even one is fine
+    ne, nb = base(synth.Q8_0, a_ne=(64, 512, 1, 1))
+    assert B.STATUS[plan(synth.Q8_0, ne, nb, a=A + 1)] == "E_LAYOUT"
+    assert plan(synth.Q8_0, ne, nb, a=A + 2) == 0
+
+
+def test_empty_and_zero_k():
+    ne, nb = base(b_ne=(0, 512, 1, 1))
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["kernel_name"] == "none"
+    # empty dst needs no pointers at all
+    assert plan(synth.F32, ne, nb, a=0, b=0, d=0) == 0
+    ne, nb = base(a_ne=(8, 0, 1, 1), b_ne=(2560, 0, 1, 1))
+    p = B.out_prod_plan(0, synth.F32, 0, D, ne, nb)
+    assert p["kernel_name"] == "zero"
+
+
+def test_range_limit():
+    ne, nb = base(b_ne=(1 << 31, 1, 1, 1), a_ne=(8, 1, 1, 1))
+    assert B.STATUS[plan(synth.F32, ne, nb)] == "E_RANGE"
+
+
+def test_kernel_choice_on_workloads():
+    want = {
+        "lora_r8_single": "skinny", "lora_r4_2560": "skinny", "lora_r24_9216": "skinny",
+        "deltanet_bcast": "tiled", "q8_0_5120": "tiled", "q4_K_5120x17408": "tiled",
+        "q4_K_17408x5120": "tiled",
+    }
+    for name, kern in want.items():
+        a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
+        ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
+        p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
+        assert p["kernel_name"] == kern, name
+        assert p["grid"] >= 1
+
+
+def test_forced_kernels():
+    ne, nb = base()
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_TILED)["kernel_name"] == "tiled"
+    ne, nb = base(synth.Q8_0, a_ne=(64, 512, 1, 1))
+    assert B.STATUS[plan(synth.Q8_0, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
+    ne, nb = base(a_ne=(33, 512, 1, 1))
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=7)] == "E_KERNEL"

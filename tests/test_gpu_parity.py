@@ -1,0 +1,268 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Gate (per element): no NaN/Inf, |gpu - ref| <= 1e-5 * sum_k |a||b|.  Integer
+inputs, one-hot b and K = 1 are checked bit for bit.  Sizes: small ragged
+shapes spanning several tiles for both kernels; every workload at full size
+in the launch configuration the benchmark uses, with the oracle on sampled
+output columns where the full oracle would take too long.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from outer_product_gemm_amd import binding as B
+from outer_product_gemm_amd import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    B.load_library()
+    yield
+
+
+def seed_of(*parts):
+    return zlib.crc32(repr(parts).encode()) & 0x7FFFFFFF
+
+
+def check_case(inst, kernel=0, cols=None):
+    G.log("case", inst.name, synth.TYPE_NAMES[inst.a_type], inst.ne[:8], "kernel", kernel)
+    gpu = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, kernel)
+    if cols is None:
+        ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
+        res = oracle.check(gpu, ref, den, TOL)
+        assert np.isfinite(gpu).all()
+    else:
+        ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, cols=cols)
+        g = np.stack([gpu[i3, i2, i1] for i1, i2, i3 in cols])
+        res = oracle.check(g, ref, den, TOL)
+        assert np.isfinite(gpu).all(), "NaN/Inf in the full GPU output"
+    G.log("   ", res)
+    assert res["ok"], res
+    return gpu
+
+
+SMALL = [
+    # (a_type, a_ne, b_ne, kernel)
+    (synth.F32, (1, 7, 1, 1), (5, 7, 1, 1), 0),
+    (synth.F32, (4, 100, 1, 1), (33, 100, 1, 1), 0),
+    (synth.F32, (8, 512, 1, 1), (100, 512, 1, 1), 0),
+    (synth.F32, (13, 33, 2, 1), (37, 33, 4, 1), 0),
+    (synth.F32, (24, 65, 1, 2), (300, 65, 1, 4), 0),
+    (synth.F32, (32, 511, 1, 1), (17, 511, 1, 1), 0),
+    (synth.F32, (16, 3, 1, 1), (16, 3, 1, 1), 0),
+    (synth.F32, (33, 17, 1, 1), (1, 17, 1, 1), 0),
+    (synth.F32, (130, 100, 2, 1), (129, 100, 4, 1), 0),
+    (synth.F32, (257, 40, 1, 2), (300, 40, 1, 2), 0),
+    (synth.F32, (128, 512, 1, 1), (128, 512, 1, 1), 0),
+    (synth.F32, (200, 1, 1, 1), (150, 1, 1, 1), 0),
+    (synth.F32, (8, 512, 1, 1), (100, 512, 1, 1), B.KERNEL_TILED),
+    (synth.F32, (24, 65, 1, 2), (300, 65, 1, 4), B.KERNEL_TILED),
+    (synth.F32, (5, 31, 3, 1), (70, 31, 6, 1), B.KERNEL_TILED),
+    (synth.Q8_0, (32, 1, 1, 1), (7, 1, 1, 1), 0),
+    (synth.Q8_0, (160, 33, 1, 1), (130, 33, 1, 1), 0),
+    (synth.Q8_0, (288, 300, 2, 1), (70, 300, 4, 1), 0),
+    (synth.Q4_K, (256, 1, 1, 1), (5, 1, 1, 1), 0),
+    (synth.Q4_K, (512, 17, 1, 1), (130, 17, 1, 1), 0),
+    (synth.Q4_K, (768, 70, 1, 2), (129, 70, 3, 2), 0),
+]
+
+
+@pytest.mark.parametrize("a_type,a_ne,b_ne,kernel", SMALL)
+def test_small_ragged(a_type, a_ne, b_ne, kernel):
+    inst = synth.make_instance("small", a_type, a_ne, b_ne, seed_of(a_type, a_ne, b_ne))
+    check_case(inst, kernel)
+
+
+def test_rank1_K1_bit_exact():
+    """K = 1: dst = RN32(a[i0]*b[i1]) exactly, on both kernels."""
+    for kernel, ne00 in ((B.KERNEL_SKINNY, 8), (B.KERNEL_TILED, 8), (B.KERNEL_TILED, 200)):
+        inst = synth.make_instance("k1", synth.F32, (ne00, 1, 1, 1), (300, 1, 1, 1), 77)
+        gpu = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, kernel)
+        expect = (inst.b[0, 0, 0][:, None].astype(np.float64) * inst.a[0, 0, 0][None, :]).astype(np.float32)
+        assert np.array_equal(gpu[0, 0], expect)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_full_size(name):
+    """Every workload at its full size, auto kernel choice (the bench's launch)."""
+    inst = synth.workload(name)
+    big = inst.ne[0] * inst.ne[1] * inst.ne[4] > 5e9
+    cols = None
+    if big:
+        rng = np.random.default_rng(seed_of(name))
+        n = inst.ne[4]
+        pick = sorted(set([0, n - 1, n // 2] + list(rng.choice(n, 13, replace=False))))
+        cols = np.array([[i1, 0, 0] for i1 in pick])
+    check_case(inst, 0, cols)
+
+
+def _int_f32(rng, shape, lim=16):
+    return rng.integers(-lim, lim + 1, size=shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("a_ne,b_ne,kernel", [
+    ((24, 512, 1, 1), (9216, 512, 1, 1), 0),         # skinny at the rank-24 shape
+    ((128, 512, 4, 1), (128, 512, 16, 1), 0),        # broadcast shape
+    ((256, 17408, 1, 1), (128, 17408, 1, 1), 0),     # long K: |sum| <= 4.46e6 < 2^24
+])
+def test_integer_exact_f32(a_ne, b_ne, kernel):
+    rng = np.random.default_rng(seed_of("int", a_ne))
+    ne, nb = synth.make_ne_nb(synth.F32, a_ne, b_ne)
+    a = _int_f32(rng, (a_ne[3], a_ne[2], a_ne[1], a_ne[0]))
+    b = _int_f32(rng, (b_ne[3], b_ne[2], b_ne[1], b_ne[0]))
+    gpu = G.run(a, synth.F32, b, ne, nb, kernel)
+    ref, _ = oracle.out_prod(a, synth.F32, b, ne, nb)
+    assert np.array_equal(gpu, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("name", ["q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120"])
+def test_integer_exact_quant(name):
+    """d = dmin = 1 and b in {-1, 0, 1}: every partial sum is an integer below
+    2^24, so the GPU must equal the oracle bit for bit at the full shape."""
+    a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
+    rng = synth.rng_for(seed_of("intq", name))
+    one = int(synth.fp16_bits([1.0])[0])
+    nrows = a_ne[1]
+    if a_type == synth.Q8_0:
+        a = synth.q8_0_rows(rng, nrows, a_ne[0], d_bits=one)
+    else:
+        a = synth.q4_K_rows(rng, nrows, a_ne[0], d_bits=one, dmin_bits=one)
+    b = rng.integers(-1, 2, size=(1, 1, b_ne[1], b_ne[0])).astype(np.float32)
+    ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
+    G.log("int-exact", name)
+    gpu = G.run(a, a_type, b, ne, nb)
+    cols = np.array([[i1, 0, 0] for i1 in (0, 1, 511, 777, b_ne[0] - 1)])
+    ref, _ = oracle.out_prod(a, a_type, b, ne, nb, cols=cols)
+    for j, (i1, _, _) in enumerate(cols):
+        assert np.array_equal(gpu[0, 0, i1], ref[j].astype(np.float32)), i1
+
+
+@pytest.mark.parametrize("name", ["q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120"])
+def test_dequant_bit_exact_one_hot(name):
+    """One-hot b picks row k of a into dst column i1, so dst = the kernel's own
+    dequantized values.  Every row of a is covered, at the full shape, and
+    must equal the oracle's decode bit for bit (as values: -0 == +0)."""
+    inst = synth.workload(name)
+    K, M, N = inst.ne[1], inst.ne[0], inst.ne[4]
+    rowb = inst.a.shape[-1]
+    expect = oracle.dequant_rows(inst.a.reshape(-1), inst.a_type, M, K, rowb)
+    a_d = G.to_dev(inst.a.reshape(-1))
+    out = torch.empty((N, M), dtype=torch.float32, device="cuda:0")
+    ne, nb = inst.ne, inst.nb
+    stream = torch.cuda.current_stream().cuda_stream
+    for start in range(0, K, N):
+        rows = np.arange(start, min(K, start + N))
+        b_d = torch.zeros((K, N), dtype=torch.float32, device="cuda:0")
+        cols = torch.arange(rows.size, device="cuda:0")
+        b_d[torch.from_numpy(rows).to("cuda:0"), cols] = 1.0
+        out.fill_(float("nan"))
+        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), ne, nb, stream)
+        got = out[: rows.size].cpu().numpy()
+        assert np.array_equal(got, expect[rows]), (name, start)
+
+
+def test_deterministic_repeat():
+    for name in ("deltanet_bcast", "lora_r24_9216", "q8_0_5120"):
+        inst = synth.workload(name)
+        g1 = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
+        g2 = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
+        assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32)), name
+
+
+def test_broadcast_invariant_gpu():
+    """Slices sharing i2/dps2 with identical b slices are bit-identical, and
+    each equals a one-slice call on (a[:,:,i2/dps2], b[:,:,i2])."""
+    inst = synth.workload("deltanet_bcast")
+    b = inst.b.copy()
+    b[0, 1] = b[0, 0]
+    b[0, 6] = b[0, 0]   # another a slice (6 // 4 = 1)
+    gpu = G.run(inst.a, inst.a_type, b, inst.ne, inst.nb)
+    assert np.array_equal(gpu[0, 0], gpu[0, 1])
+    assert not np.array_equal(gpu[0, 0], gpu[0, 6])
+    ne1, nb1 = synth.make_ne_nb(synth.F32, (128, 512, 1, 1), (128, 512, 1, 1))
+    for i2 in (0, 5, 15):
+        one = G.run(np.ascontiguousarray(inst.a[:, i2 // 4]), synth.F32,
+                    np.ascontiguousarray(b[:, i2]), ne1, nb1)
+        assert np.array_equal(one[0, 0], gpu[0, i2])
+
+
+def test_strided_views_and_misalignment():
+    """Padded rows and slices for a, b and dst; b and a 4-byte (not 16-byte)
+    aligned; a stride-0 broadcast of a's slices."""
+    rng = np.random.default_rng(21)
+    for a_type, ne00 in ((synth.F32, 12), (synth.F32, 150), (synth.Q8_0, 64), (synth.Q4_K, 256)):
+        K, ne02, ne10, ne12 = 37, 2, 70, 4
+        if a_type == synth.F32:
+            row = 4 * ne00 + 4 * 5                    # 5 floats of padding
+        else:
+            row = synth.row_bytes(a_type, ne00) + 8
+        nb_a = [synth.BLOCK_BYTES[a_type], row, row * K + 12, 0]
+        abytes = 4 + row * K * ne02 + 12 * ne02 + 64
+        a = np.zeros(abytes, dtype=np.uint8)
+        for s in range(ne02):
+            for k in range(K):
+                off = 4 + s * nb_a[2] + k * row
+                if a_type == synth.F32:
+                    a[off:off + 4 * ne00] = rng.standard_normal(ne00).astype(np.float32).view(np.uint8)
+                else:
+                    a[off:off + synth.row_bytes(a_type, ne00)] = synth.quant_rows(rng, a_type, 1, ne00)[0]
+        a = a[4:]
+        nb_b = [4, 4 * ne10 + 8, (4 * ne10 + 8) * K + 4, 0]
+        b = np.zeros((nb_b[2] * ne12 + 16) // 4 + 1, dtype=np.float32)
+        b[:] = rng.standard_normal(b.size).astype(np.float32)
+        nb_d = [4, 4 * ne00 + 12, (4 * ne00 + 12) * ne10 + 4, 0]
+        ne = [ne00, K, ne02, 1, ne10, K, ne12, 1, ne00, ne10, ne12, 1]
+        nb = nb_a + nb_b + nb_d
+        # device bases 4 bytes past a 256-byte boundary: no 16-byte vector loads
+        gpu = G.run(a, a_type, b, ne, nb, a_off=4, b_off=4)
+        ref, den = oracle.out_prod(a, a_type, b, ne, nb)
+        res = oracle.check(gpu, ref, den, TOL)
+        G.log("strided", synth.TYPE_NAMES[a_type], ne00, res)
+        assert res["ok"], res
+    # stride-0 broadcast of a over ne02
+    inst = synth.make_instance("s0", synth.F32, (40, 50, 1, 1), (60, 50, 3, 1), 5)
+    ne = list(inst.ne)
+    nb = list(inst.nb)
+    ne[2], nb[2] = 3, 0
+    gpu = G.run(inst.a, synth.F32, inst.b, ne, nb)
+    ref, den = oracle.out_prod(inst.a, synth.F32, inst.b, ne, nb)
+    assert oracle.check(gpu, ref, den, TOL)["ok"]
+
+
+def test_zero_K_and_empty_and_errors():
+    ne, nb = synth.make_ne_nb(synth.F32, (8, 0, 1, 1), (100, 0, 1, 1))
+    out = torch.full((100, 8), float("nan"), device="cuda:0")
+    B.out_prod(0, synth.F32, 0, out.data_ptr(), ne, nb, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    # empty dst: nothing happens
+    ne, nb = synth.make_ne_nb(synth.F32, (8, 10, 1, 1), (0, 10, 1, 1))
+    B.out_prod(0, synth.F32, 0, 0, ne, nb, 0)
+    # an error leaves dst untouched
+    inst = synth.workload("lora_r8_single")
+    a_d, b_d = G.to_dev(inst.a), G.to_dev(inst.b)
+    out = torch.full((2560, 8), 7.0, device="cuda:0")
+    ne = list(inst.ne)
+    ne[5] = 511
+    st = B.out_prod_status(a_d.data_ptr(), synth.F32, b_d.data_ptr(), out.data_ptr(), ne, inst.nb,
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert B.STATUS[st] == "E_K" and (out == 7.0).all()
+
+
+def test_tensor_helper_matches_raw_call():
+    inst = synth.workload("deltanet_bcast")
+    a_d, b_d = G.to_dev(inst.a), G.to_dev(inst.b)
+    out = B.out_prod_tensors(a_d, synth.F32, b_d)
+    torch.cuda.synchronize()
+    raw = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
+    assert np.array_equal(out.cpu().numpy(), raw)
