@@ -113,7 +113,7 @@ def main():
     flops_step = sum(w[0] for w in work)
     bytes_step = sum(w[1] for w in work)
     set_bytes = sum(i.a.nbytes + i.b.nbytes + 4 * int(np.prod(i.dst_shape)) for i in insts)
-    R = args.rotate or max(1, min(8, int(np.ceil(600e6 / set_bytes))))
+    R = args.rotate or max(1, min(256, int(np.ceil(600e6 / set_bytes))))
 
     sets = []
     for r in range(R):
@@ -170,11 +170,13 @@ def main():
     ai = flops_step / bytes_step
     bound = "mfma" if ai >= RIDGE else "hbm"
     kernels = sorted(set(p[3]["kernel_name"] for p in sets[0]))
+    # algorithmic work per launch / the kernel's average launch duration
+    mean_s = float(per_launch.mean()) * 1e-3
     if bound == "mfma":
-        achieved = float(np.mean(flops_launch / (avg_ms * 1e-3)) / 1e12)
+        achieved = float(flops_launch.mean()) / mean_s / 1e12
         peak, unit = PEAK_MFMA_F32_TFLOPS, "TFLOP/s"
     else:
-        achieved = float(np.mean(bytes_launch / (avg_ms * 1e-3)) / 1e9)
+        achieved = float(bytes_launch.mean()) / mean_s / 1e9
         peak, unit = PEAK_HBM_GBPS, "GB/s"
     src_hash = kernel_source_hash()
     traffic = None
@@ -185,7 +187,8 @@ def main():
         "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
         "frac": round(achieved / peak, 4), "traffic": traffic,
         "kernel": kernels[0] if len(kernels) == 1 else kernels,
-        "avg_launch_us": [round(float(x) * 1e3, 2) for x in avg_ms],
+        "avg_launch_us": round(mean_s * 1e6, 2),
+        "avg_launch_us_by_launch": [round(float(x) * 1e3, 2) for x in avg_ms],
         "algorithmic_flops_per_launch": [int(x) for x in flops_launch],
         "algorithmic_bytes_per_launch": [int(x) for x in bytes_launch],
     }

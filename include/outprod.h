@@ -87,9 +87,12 @@ int out_prod(const void *a, int a_type, const float *b, float *dst,
 
 /* Kernel families (for out_prod_plan's report and out_prod_ex's override). */
 #define OUTPROD_KERNEL_AUTO 0   /* let the library choose */
-#define OUTPROD_KERNEL_SKINNY 1 /* f32 a, ne00 <= 32: bandwidth-bound MFMA 16x16x4 column
-                                   kernel, K split over the waves of a workgroup */
-#define OUTPROD_KERNEL_TILED 2  /* LDS-staged fp32 tiles, MFMA 32x32x2, any a type/shape */
+#define OUTPROD_KERNEL_SKINNY 1 /* f32 a only: MFMA 16x16x4 column kernel, 16 x 16*MT
+                                   dst tiles, K split over the waves of a workgroup; chosen
+                                   for ne00 <= 32 (bandwidth-bound rank-r gradients) and for
+                                   f32 problems with too few output tiles for the tiled kernel */
+#define OUTPROD_KERNEL_TILED 2  /* LDS-staged fp32 tiles, MFMA 32x32x2 or 16x16x4, any a
+                                   type and shape; a menu of tile configurations */
 #define OUTPROD_KERNEL_ZERO 3   /* K == 0: writes zeros */
 #define OUTPROD_KERNEL_NONE 4   /* empty dst: nothing to do */
 
@@ -106,6 +109,7 @@ typedef struct outprod_plan {
     int64_t dps2;     /* ne12 / ne02 */
     int64_t dps3;     /* ne13 / ne03 */
     int64_t flops;    /* 2 * ne00 * ne10 * K * slices */
+    int variant;      /* configuration index within the family */
 } outprod_plan;
 
 /*
@@ -122,8 +126,11 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
 /*
  * out_prod_ex: out_prod with the kernel family forced (OUTPROD_KERNEL_AUTO,
  * _SKINNY or _TILED), for A/B measurements and for testing both kernels on
- * the same problem.  A family that cannot run the problem returns
- * OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a or ne00 > 32).
+ * the same problem.  Bits 8-15 of `kernel` may force a configuration of the
+ * family: (index + 1) << 8, with the index as reported in
+ * outprod_plan.variant; 0 lets the library choose.  A family or
+ * configuration that cannot run the problem returns OUTPROD_E_KERNEL (e.g.
+ * SKINNY for a quantized a, or a configuration index with SKINNY).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);

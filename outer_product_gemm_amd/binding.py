@@ -36,6 +36,12 @@ STATUS = {
 KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
 
+
+def kernel_code(family: int, config: int = None) -> int:
+    """out_prod_ex's kernel argument: a family, optionally with a forced
+    configuration index (as reported by out_prod_plan's ``variant``)."""
+    return family | ((config + 1) << 8 if config is not None else 0)
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
 
 # Every symbol the header declares.
@@ -52,7 +58,7 @@ class outprod_plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
                 ("tile_k", ctypes.c_int), ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
-                ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64)]
+                ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int)]
 
 
 _I64x12 = ctypes.c_int64 * 12

@@ -79,8 +79,8 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
 
     const bool empty = ne00 == 0 || ne10 == 0 || ne12 == 0 || ne13 == 0;
     if (empty) {
-        if (kernel != OUTPROD_KERNEL_AUTO && kernel != OUTPROD_KERNEL_SKINNY &&
-            kernel != OUTPROD_KERNEL_TILED)
+        const int fam = kernel & 0xFF;
+        if (fam != OUTPROD_KERNEL_AUTO && fam != OUTPROD_KERNEL_SKINNY && fam != OUTPROD_KERNEL_TILED)
             return OUTPROD_E_KERNEL;
         l.kernel = OUTPROD_KERNEL_NONE;
         return OUTPROD_OK;
@@ -152,18 +152,33 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     p.vec_b = (uintptr_t)b % 16 == 0 && nb[5] % 16 == 0 && nb[6] % 16 == 0 && nb[7] % 16 == 0;
 
     if (K == 0) {
-        if (kernel != OUTPROD_KERNEL_AUTO && kernel != OUTPROD_KERNEL_SKINNY &&
-            kernel != OUTPROD_KERNEL_TILED)
+        const int fam = kernel & 0xFF;
+        if (fam != OUTPROD_KERNEL_AUTO && fam != OUTPROD_KERNEL_SKINNY && fam != OUTPROD_KERNEL_TILED)
             return OUTPROD_E_KERNEL;
         plan_zero(p, &l);
         return l.grid > lim ? OUTPROD_E_RANGE : OUTPROD_OK;
     }
 
+    // kernel = family | (tile configuration + 1) << 8; configuration 0 = automatic
+    const int variant = (kernel >> 8) & 0xFF;
+    kernel &= 0xFF;
+    if (variant != 0 && kernel != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
+    l.variant = variant;
     bool ok;
     switch (kernel) {
-    case OUTPROD_KERNEL_AUTO:
-        ok = plan_skinny(p, &l) || plan_tiled(p, &l);
+    case OUTPROD_KERNEL_AUTO: {
+        // narrow f32 a, or an f32 problem with too few output tiles to fill
+        // the chip: the column kernel; everything else: the tiled kernel
+        Launch t = l;
+        const bool tiled_ok = plan_tiled(p, &t);
+        if (p.a_type == OUTPROD_TYPE_F32 && (p.M <= 32 || !tiled_ok || t.grid < 128)) {
+            ok = plan_skinny(p, &l);
+        } else {
+            l = t;
+            ok = tiled_ok;
+        }
         break;
+    }
     case OUTPROD_KERNEL_SKINNY:
         ok = plan_skinny(p, &l);
         break;
@@ -236,6 +251,7 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
     plan->dps2 = c.p.dps2;
     plan->dps3 = c.p.dps3;
     plan->flops = 2 * c.p.M * c.p.N * c.p.K * plan->slices;
+    plan->variant = c.l.variant;
     return OUTPROD_OK;
 }
 

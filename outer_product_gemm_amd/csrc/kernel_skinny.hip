@@ -1,17 +1,21 @@
-// kernel_skinny.hip -- OUT_PROD for narrow f32 a (ne00 <= 32): the LoRA
+// kernel_skinny.hip -- OUT_PROD for f32 a with few output tiles: the LoRA
 // parameter gradients of rank 4/8/24 (pages: "metal: OUT_PROD runs batched,
 // broadcast and narrow shapes on the GPU", body: the rank gradients at the 4B's
-// shapes).  These shapes move b once and do a handful of flops per byte, so
-// they are bound by HBM bandwidth and by how fast the chip fills with loads.
+// shapes) and small per-head products such as the delta-net backward (same
+// page: 16 value heads over 4 key heads).  The rank-r shapes move b once and
+// do a handful of flops per byte, so they are bound by HBM bandwidth and by
+// how fast the chip fills with loads; the per-head shapes have too few
+// 128 x 128 tiles to occupy 256 CUs.
 //
 // Decomposition: one workgroup per 16 consecutive columns i1 of b (64 bytes of
-// every row k) in one dst slice, all K rows.  Its W waves take interleaved
-// 4-row steps of K.  Each step is one v_mfma_f32_16x16x4_f32 whose A operand is
-// read straight from b (lane l: b[k0 + l/16][n0 + l%16]) and whose B operand is
-// read straight from a (lane l: a[k0 + l/16][16t + l%16]); the MFMA performs the
-// k reduction inside the instruction.  The W per-wave partial tiles are then
-// summed in LDS in wave order, so the result is deterministic and every dst
-// element has one writer.  No workspace, no atomics.
+// every row k) and 16*MT consecutive columns i0 of a, in one dst slice, all K
+// rows.  Its W waves take interleaved 4-row steps of K.  Each step is one
+// v_mfma_f32_16x16x4_f32 per 16 columns of a, whose A operand is read
+// straight from b (lane l: b[k0 + l/16][n0 + l%16]) and whose B operand is
+// read straight from a (lane l: a[k0 + l/16][m0 + 16t + l%16]); the MFMA
+// performs the k reduction inside the instruction.  The W per-wave partial
+// tiles are then summed in LDS in wave order, so the result is deterministic
+// and every dst element has one writer.  No workspace, no atomics.
 #include "kernel_common.h"
 #include "outprod.h"
 
@@ -22,12 +26,14 @@ constexpr int kSkinnyCols = 16;  // columns i1 per workgroup
 constexpr int kUnroll = 8;       // 4-row steps whose loads are issued together
 
 template <int MT, int W>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks) {
+__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks, int m_blocks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int z = logical / col_blocks;
     const int n0 = (logical % col_blocks) * kSkinnyCols;
+    const int rest = logical / col_blocks;
+    const int m0 = (rest % m_blocks) * 16 * MT;
+    const int z = rest / m_blocks;
     const SliceBase s = slice_base(p, z);
 
     const int K = (int)p.K, M = (int)p.M;
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
     bool a_ok[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const int i0 = 16 * t + (lane & 15);
+        const int i0 = m0 + 16 * t + (lane & 15);
         a_ok[t] = i0 < M;
         acol[t] = s.a + (int64_t)i0 * 4;
     }
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
 #pragma unroll
         for (int w = 0; w < W; ++w) sum += red[w][t][r][l];
         const int i1 = n0 + 4 * (l >> 4) + r;
-        const int i0 = 16 * t + (l & 15);
+        const int i0 = m0 + 16 * t + (l & 15);
         if (i1 < p.N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
     }
 }
@@ -92,9 +98,10 @@ constexpr int kSkinnyWaves = 8;
 }  // namespace
 
 bool plan_skinny(const Problem &p, Launch *l) {
-    if (p.a_type != OUTPROD_TYPE_F32 || p.M > 32 || p.M < 1) return false;
+    if (p.a_type != OUTPROD_TYPE_F32 || p.M < 1) return false;
     const int64_t col_blocks = (p.N + kSkinnyCols - 1) / kSkinnyCols;
     const int mt = p.M > 16 ? 2 : 1;
+    const int64_t m_blocks = (p.M + 16 * mt - 1) / (16 * mt);
     l->kernel = OUTPROD_KERNEL_SKINNY;
     l->variant = mt;
     l->tile_m = 16 * mt;
@@ -102,14 +109,15 @@ bool plan_skinny(const Problem &p, Launch *l) {
     l->tile_k = 4;
     l->block = 64 * kSkinnyWaves;
     l->lds_bytes = kSkinnyWaves * mt * 256 * 4;
-    l->grid = col_blocks * p.ne12 * p.ne13;
+    l->grid = col_blocks * m_blocks * p.ne12 * p.ne13;
     return true;
 }
 
 hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s) {
     int col_blocks = (int)((p.N + kSkinnyCols - 1) / kSkinnyCols);
+    int m_blocks = (int)((p.M + l.tile_m - 1) / l.tile_m);
     Problem pp = p;
-    void *args[] = {&pp, &col_blocks};
+    void *args[] = {&pp, &col_blocks, &m_blocks};
     const void *fn = l.variant == 2 ? (const void *)&skinny_kernel<2, kSkinnyWaves>
                                     : (const void *)&skinny_kernel<1, kSkinnyWaves>;
     return hipLaunchKernel(fn, dim3((unsigned)l.grid), dim3(l.block), args, 0, s);

@@ -1,23 +1,25 @@
-// kernel_tiled.hip -- OUT_PROD for wide problems: the grouped-head broadcast
-// backward and frozen quantized weight x f32 gradient products (pages: "metal:
+// kernel_tiled.hip -- OUT_PROD for wide problems: frozen quantized weight x f32
+// gradient products and other shapes with many flops per byte (pages: "metal:
 // OUT_PROD runs batched, broadcast and narrow shapes on the GPU" -- every
 // (i2, i3) slice in one launch instead of one encode per slice; "metal:
 // OUT_PROD multiplies in float staging" -- fp32 staging of both operands; and
 // the MUL_MAT_ID_BACK page's note that quantized rows are dequantized in
-// registers rather than copied).
+// registers rather than copied to a scratch buffer).
 //
 // In BLAS terms each slice is dst(N x M, row-major) = B^T A with A = a's
 // [K][M] rows and B = b's [K][N] rows: both operands are K-major, so a K-tile
 // of either is BK contiguous row segments.  A workgroup owns a BM x BN dst
 // tile (BM along i0, BN along i1) of one slice and walks K in BK-row stages:
 //   global -> registers (a: f32 copy or q8_0/q4_K block decode to fp32;
-//   b: f32) -> LDS [k][i0] / [k][i1] (fp32, double buffered) ->
-//   v_mfma_f32_32x32x2_f32 with fp32 accumulators.
-// The next stage's global loads are issued before the current stage's MFMAs
-// so their latency hides behind matrix work; one barrier per stage.
+//   b: f32) -> LDS [k][i0] / [k][i1] (fp32, two buffers) ->
+//   v_mfma_f32_{32x32x2,16x16x4}_f32 with fp32 accumulators.
+// Pipeline: the registers hold stage t+1 while stage t is multiplied; halfway
+// through stage t's MFMAs they are decoded into the other LDS buffer and the
+// loads of stage t+2 are issued, so a global load has a whole stage of matrix
+// work to arrive.  One barrier per stage.
 // MFMA operand roles: A operand (rows) = b values -> dst rows i1;
-// B operand (columns) = a values -> dst columns i0, so the lanes of a
-// 32-wide accumulator column write 32 consecutive floats of a dst row.
+// B operand (columns) = a values -> dst columns i0, so the lanes of one
+// accumulator row write consecutive floats of a dst row.
 #include "kernel_common.h"
 #include "outprod.h"
 
@@ -25,20 +27,23 @@ namespace outprod {
 namespace {
 
 // ---------------------------------------------------------------- loaders
+// Each loader moves a BK x BW tile (BW columns of BK consecutive K rows) of
+// one operand: load() issues the global reads of a stage into registers,
+// store() converts them to fp32 and writes the LDS tile [k][column].
+// Work is split into groups (4 floats, or 8 quantized values); thread tid
+// takes groups tid, tid+T, ...; the last round is guarded when T does not
+// divide the group count.
 
-// f32 K-major operand (a or b): BK x BW tile as float4 groups.
 template <int BW, int BK, int T>
 struct F32Loader {
-    static constexpr int kGroups = BK * BW / 4 / T;
-    static_assert(kGroups * 4 * T == BK * BW, "tile must split evenly into float4 groups");
-    const uint8_t *base;  // slice base + column offset of this thread's groups
-    int64_t ld;           // row stride in bytes
-    int w0;               // first column of the tile
-    int W;                // operand width (M or N)
-    int K;
+    static constexpr int kGroups = BK * BW / 4;
+    static constexpr int kPer = (kGroups + T - 1) / T;
+    static_assert(BW % 4 == 0, "tile width must be a multiple of 4");
+    const uint8_t *base;
+    int64_t ld;
+    int w0, W, K, tid;
     bool vec;
-    int tid;
-    floatx4 r[kGroups];
+    floatx4 r[kPer];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool vec_ok, int t) {
@@ -52,13 +57,13 @@ struct F32Loader {
     }
     __device__ void load(int k0) {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
             const int row = g / (BW / 4), c = w0 + 4 * (g % (BW / 4));
             const int k = k0 + row;
-            const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)c * 4;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if (k < K) {
+            if ((kGroups % T == 0 || g < kGroups) && k < K) {
+                const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)c * 4;
                 if (vec && c + 3 < W) {
                     v = *(const floatx4 *)ptr;
                 } else {
@@ -73,25 +78,28 @@ struct F32Loader {
     template <int LD>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
-            const int row = g / (BW / 4), c = 4 * (g % (BW / 4));
-            *(floatx4 *)&lds[row][c] = r[j];
+            if (kGroups % T == 0 || g < kGroups) {
+                const int row = g / (BW / 4), c = 4 * (g % (BW / 4));
+                *(floatx4 *)&lds[row][c] = r[j];
+            }
         }
     }
 };
 
-// q8_0 a: groups of 8 consecutive values of one block.  34-byte blocks are
-// only 2-byte aligned, so bytes come in as 16-bit loads.
+// q8_0 a: groups of 8 consecutive values of one 32-value block.  34-byte
+// blocks are only 2-byte aligned, so the codes come in as 16-bit loads.
 template <int BM, int BK, int T>
 struct Q8Loader {
-    static constexpr int kGroups = BK * BM / 8 / T;
-    static_assert(kGroups * 8 * T == BK * BM, "tile must split evenly into 8-value groups");
+    static constexpr int kGroups = BK * BM / 8;
+    static constexpr int kPer = (kGroups + T - 1) / T;
+    static_assert(BM % 8 == 0, "tile width must be a multiple of 8");
     const uint8_t *base;
     int64_t ld;
     int m0, M, K, tid;
-    uint32_t d[kGroups];
-    uint32_t q[kGroups][4];
+    uint32_t d[kPer];
+    uint32_t q[kPer][4];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool, int t) {
@@ -104,13 +112,13 @@ struct Q8Loader {
     }
     __device__ void load(int k0) {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             d[j] = 0;
             q[j][0] = q[j][1] = q[j][2] = q[j][3] = 0;
-            if (k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 5) * 34;
                 const uint16_t *qs = (const uint16_t *)(blk + 2 + (m & 31));
                 d[j] = *(const uint16_t *)blk;
@@ -122,26 +130,20 @@ struct Q8Loader {
     template <int LD>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
+            if (!(kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             const float dd = half_bits_to_float(d[j]);
-            floatx4 lo, hi;
+            float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // value = d * q, exact in fp32 (11 + 7 significant bits)
-                const float q0 = (float)(int8_t)(q[j][e] & 0xFFu);
-                const float q1 = (float)(int8_t)(q[j][e] >> 8);
-                if (e < 2) {
-                    lo[2 * e] = dd * q0;
-                    lo[2 * e + 1] = dd * q1;
-                } else {
-                    hi[2 * e - 4] = dd * q0;
-                    hi[2 * e - 3] = dd * q1;
-                }
+                v[2 * e] = dd * (float)(int8_t)(q[j][e] & 0xFFu);
+                v[2 * e + 1] = dd * (float)(int8_t)(q[j][e] >> 8);
             }
-            *(floatx4 *)&lds[row][c] = lo;
-            *(floatx4 *)&lds[row][c + 4] = hi;
+            *(floatx4 *)&lds[row][c] = floatx4{v[0], v[1], v[2], v[3]};
+            *(floatx4 *)&lds[row][c + 4] = floatx4{v[4], v[5], v[6], v[7]};
         }
     }
 };
@@ -149,12 +151,13 @@ struct Q8Loader {
 // q4_K a: groups of 8 consecutive values of one 32-value sub-block.
 template <int BM, int BK, int T>
 struct Q4KLoader {
-    static constexpr int kGroups = BK * BM / 8 / T;
-    static_assert(kGroups * 8 * T == BK * BM, "tile must split evenly into 8-value groups");
+    static constexpr int kGroups = BK * BM / 8;
+    static constexpr int kPer = (kGroups + T - 1) / T;
+    static_assert(BM % 8 == 0, "tile width must be a multiple of 8");
     const uint8_t *base;
     int64_t ld;
     int m0, M, K, tid;
-    uint32_t dd[kGroups], s0[kGroups], s1[kGroups], s2[kGroups], q0[kGroups], q1[kGroups];
+    uint32_t dd[kPer], s0[kPer], s1[kPer], s2[kPer], q0[kPer], q1[kPer];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool, int t) {
@@ -167,12 +170,12 @@ struct Q4KLoader {
     }
     __device__ void load(int k0) {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             dd[j] = s0[j] = s1[j] = s2[j] = q0[j] = q1[j] = 0;
-            if (k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 8) * 144;
                 const int w = m & 255, sub = w >> 5, pos = w & 31;
                 const uint32_t *hdr = (const uint32_t *)blk;
@@ -189,12 +192,15 @@ struct Q4KLoader {
     template <int LD>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kGroups; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
+            if (!(kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             const int sub = ((m0 + c) & 255) >> 5;
             // 6-bit scale and min of sub-block `sub` from the 12 packed bytes
-            // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2).
+            // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2): for sub < 4 the low 6
+            // bits of bytes sub and 4+sub; otherwise the nibbles of byte
+            // 8+(sub-4) below the top two bits of bytes sub-4 and sub.
             uint32_t sc, mn;
             if (sub < 4) {
                 sc = (s0[j] >> (8 * sub)) & 0x3Fu;
@@ -202,23 +208,23 @@ struct Q4KLoader {
             } else {
                 const int sh = 8 * (sub - 4);
                 const uint32_t lo = (s2[j] >> sh) & 0xFFu;
-                sc = (lo & 0x0Fu) | (((s0[j] >> sh) >> 6 & 0x3u) << 4);
-                mn = (lo >> 4) | (((s1[j] >> sh) >> 6 & 0x3u) << 4);
+                sc = (lo & 0x0Fu) | ((((s0[j] >> sh) >> 6) & 0x3u) << 4);
+                mn = (lo >> 4) | ((((s1[j] >> sh) >> 6) & 0x3u) << 4);
             }
             const float d = half_bits_to_float(dd[j] & 0xFFFFu);
             const float dmin = half_bits_to_float(dd[j] >> 16);
             const float ds = d * (float)sc;    // exact: <= 17 significant bits
             const float dm = dmin * (float)mn; // exact
             const int shift = (sub & 1) ? 4 : 0;
-            floatx4 lo4, hi4;
+            float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // value = d*sc*q - dmin*m: the product is exact, one rounding
-                lo4[e] = ds * (float)((q0[j] >> (8 * e + shift)) & 0xFu) - dm;
-                hi4[e] = ds * (float)((q1[j] >> (8 * e + shift)) & 0xFu) - dm;
+                v[e] = ds * (float)((q0[j] >> (8 * e + shift)) & 0xFu) - dm;
+                v[4 + e] = ds * (float)((q1[j] >> (8 * e + shift)) & 0xFu) - dm;
             }
-            *(floatx4 *)&lds[row][c] = lo4;
-            *(floatx4 *)&lds[row][c + 4] = hi4;
+            *(floatx4 *)&lds[row][c] = floatx4{v[0], v[1], v[2], v[3]};
+            *(floatx4 *)&lds[row][c + 4] = floatx4{v[4], v[5], v[6], v[7]};
         }
     }
 };
@@ -238,18 +244,51 @@ struct ALoaderFor<OUTPROD_TYPE_Q4_K, BM, BK, T> {
     typedef Q4KLoader<BM, BK, T> type;
 };
 
+// ---------------------------------------------------------------- MFMA shapes
+// fp32 MFMA, lane l of the wave:
+//   32x32x2: supplies A[l%32][k=l/32], B[k=l/32][l%32]; accumulator register r
+//            holds D[8*(r/4) + 4*(l/32) + r%4][l%32]            (16 registers)
+//   16x16x4: supplies A[l%16][k=l/16], B[k=l/16][l%16]; register r holds
+//            D[4*(l/16) + r][l%16]                             (4 registers)
+template <int MF>
+struct Mfma;
+template <>
+struct Mfma<32> {
+    typedef floatx16 acc_t;
+    static constexpr int KS = 2, NR = 16;
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+};
+template <>
+struct Mfma<16> {
+    typedef floatx4 acc_t;
+    static constexpr int KS = 4, NR = 4;
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row(int r, int lane) { return 4 * (lane >> 4) + r; }
+};
+
+// LDS row length: the MF-lane groups of one operand read (rows k, k+1, ...)
+// start in different banks.
+__host__ __device__ constexpr int lds_ld(int bw, int mf) {
+    return bw + (((mf == 32 ? 32 : 16) - bw % 64) % 64 + 64) % 64;
+}
+
 // ---------------------------------------------------------------- kernel
 
-template <int AT, int BM, int BN, int BK, int WGM, int WGN>
+template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK>
 __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int tiles_m,
                                                                int tiles_n) {
+    typedef Mfma<MF> MM;
     constexpr int T = 64 * WGM * WGN;
-    constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int LDA = BM + 32, LDB = BN + 32;  // +32 floats: the two half-waves
-                                                 // of an operand read use other banks
-    static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
-    static_assert(BK % 2 == 0, "BK must be even");
+    constexpr int WTM = MF * FM, WTN = MF * FN;
+    constexpr int BM = WTM * WGM, BN = WTN * WGN;
+    constexpr int LDA = lds_ld(BM, MF), LDB = lds_ld(BN, MF);
+    constexpr int S = BK / MM::KS;  // MFMA steps per stage
+    static_assert(BK % MM::KS == 0 && S % 2 == 0, "stage must hold an even number of MFMA steps");
     __shared__ __attribute__((aligned(16))) float As[2][BK][LDA];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDB];
 
@@ -267,60 +306,78 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int ti
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, p.nb11, N, K, n0, p.vec_b, tid);
 
-    floatx16 acc[FM][FN];
+    typename MM::acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
 
     const int ktiles = (K + BK - 1) / BK;
     la.load(0);
     lb.load(0);
     la.store(As[0]);
     lb.store(Bs[0]);
+    if (ktiles > 1) {
+        la.load(BK);
+        lb.load(BK);
+    }
     __syncthreads();
 
-    const int half = lane >> 5, col = lane & 31;
-    for (int t = 0; t < ktiles; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < ktiles;
-        if (more) {
-            la.load((t + 1) * BK);
-            lb.load((t + 1) * BK);
-        }
+    const int kq = lane / MF, col = lane % MF;
+    const int a_col = wm * WTM + col, b_col = wn * WTN + col;
+
+    // MFMA steps [s0, s1) of a stage.  Operand fragments are double-buffered
+    // in registers: step st+1's LDS reads are issued before step st's MFMAs.
+    auto mfma_steps = [&](int cur, int s0, int s1) {
+        float af[2][FM], bf[2][FN];
 #pragma unroll
-        for (int kp = 0; kp < BK / 2; ++kp) {
-            const int kr = 2 * kp + half;
-            float af[FM], bf[FN];
+        for (int i = 0; i < FM; ++i) af[0][i] = As[cur][MM::KS * s0 + kq][a_col + MF * i];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = As[cur][kr][wm * WTM + 32 * i + col];
+        for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][MM::KS * s0 + kq][b_col + MF * j];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = Bs[cur][kr][wn * WTN + 32 * j + col];
+        for (int st = s0; st < s1; ++st) {
+            const int x = (st - s0) & 1;
+            if (st + 1 < s1) {
+                const int kr = MM::KS * (st + 1) + kq;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[j], af[i], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
         }
-        if (more) {
+    };
+
+    for (int t = 0; t < ktiles; ++t) {
+        const int cur = t & 1;
+        mfma_steps(cur, 0, S / 2);
+        if (t + 1 < ktiles) {
+            // registers hold stage t+1: decode into the free buffer, then
+            // start stage t+2's loads
             la.store(As[cur ^ 1]);
             lb.store(Bs[cur ^ 1]);
+            if (t + 2 < ktiles) {
+                la.load((t + 2) * BK);
+                lb.load((t + 2) * BK);
+            }
         }
+        mfma_steps(cur, S / 2, S);
         __syncthreads();
     }
 
-    // Accumulator register r of lane l: row 8*(r/4) + 4*(l/32) + r%4 (i1),
-    // column l%32 (i0) of the 32x32 block.
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int i0 = m0 + wm * WTM + 32 * i + col;
+        const int i0 = m0 + a_col + MF * i;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i1 = n0 + wn * WTN + 32 * j + 8 * (r >> 2) + 4 * half + (r & 3);
+            for (int r = 0; r < MM::NR; ++r) {
+                const int i1 = n0 + wn * WTN + MF * j + MM::row(r, lane);
                 if (i0 < M && i1 < N)
                     *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = acc[i][j][r];
             }
@@ -328,30 +385,101 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int ti
     }
 }
 
-// Tile configurations.
+// ---------------------------------------------------------------- configurations
+
 struct TileCfg {
-    int bm, bn, bk, wgm, wgn;
+    int mf, fm, fn, wgm, wgn, bk;
+    // Measured rate of the configuration on MI355X (tile area x K per us on
+    // the busiest CU, from the q4_K/q8_0 27B-shape sweeps); the planner
+    // compares (tiles per CU x tile area) / eff across configurations.
+    float eff;
+    int bm() const { return mf * fm * wgm; }
+    int bn() const { return mf * fn * wgn; }
+    int threads() const { return 64 * wgm * wgn; }
 };
-constexpr TileCfg kCfg0 = {128, 128, 16, 2, 2};
+
+// 0: 128 x 128, 4 waves of 64 x 64 (32x32x2) -- general purpose
+// 1: 160 x 128, 8 waves of 80 x 32 (16x16x4) -- m5120 x n1024 in 256 tiles
+// 2: 160 x 64,  4 waves of 80 x 32 (16x16x4) -- m5120 x n1024 in 512 tiles
+// 3: 272 x 128, 8 waves of 272 x 16 (16x16x4) -- m17408 x n1024 in 512 tiles
+// 4: 64 x 64,   4 waves of 32 x 32 (32x32x2) -- medium problems
+// 5: 272 x 64,  4 waves of 272 x 16 (16x16x4) -- m17408 x n1024 in 1024 tiles
+// 6: 256 x 128, 8 waves of 64 x 64 (32x32x2)
+// 7: 128 x 128, 4 waves of 64 x 64 (32x32x2), 32-row stages
+// 8: as 1 with 32-row stages
+// 9: as 3 with 32-row stages
+constexpr TileCfg kCfgs[] = {
+    {32, 2, 2, 2, 2, 16, 12.4f},
+    {16, 5, 2, 2, 4, 16, 11.5f},
+    {16, 5, 2, 2, 2, 16, 10.4f},
+    {16, 17, 1, 1, 8, 16, 12.0f},
+    {32, 1, 1, 2, 2, 16, 10.6f},
+    {16, 17, 1, 1, 4, 16, 9.8f},
+    {32, 2, 2, 4, 2, 16, 12.4f},
+    {32, 2, 2, 2, 2, 32, 12.0f},
+    {16, 5, 2, 2, 4, 32, 12.2f},
+    {16, 17, 1, 1, 8, 32, 12.1f},
+};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+template <int AT, int C>
+const void *cfg_fn() {
+    constexpr TileCfg c = kCfgs[C];
+    return (const void *)&tiled_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk>;
+}
 
 template <int AT>
 const void *tiled_fn(int variant) {
-    (void)variant;
-    return (const void *)&tiled_kernel<AT, kCfg0.bm, kCfg0.bn, kCfg0.bk, kCfg0.wgm, kCfg0.wgn>;
+    switch (variant) {
+    case 1: return cfg_fn<AT, 1>();
+    case 2: return cfg_fn<AT, 2>();
+    case 3: return cfg_fn<AT, 3>();
+    case 4: return cfg_fn<AT, 4>();
+    case 5: return cfg_fn<AT, 5>();
+    case 6: return cfg_fn<AT, 6>();
+    case 7: return cfg_fn<AT, 7>();
+    case 8: return cfg_fn<AT, 8>();
+    case 9: return cfg_fn<AT, 9>();
+    default: return cfg_fn<AT, 0>();
+    }
+}
+
+// Estimated time of a configuration: the busiest CU runs ceil(tiles / 256)
+// tiles' worth of MFMA work at the configuration's efficiency.
+double cfg_cost(const TileCfg &c, const Problem &p) {
+    const int64_t tiles = ((p.M + c.bm() - 1) / c.bm()) * ((p.N + c.bn() - 1) / c.bn()) * p.ne12 * p.ne13;
+    const int64_t per_cu = (tiles + 255) / 256;
+    return (double)per_cu * c.bm() * c.bn() / c.eff;
 }
 
 }  // namespace
 
 bool plan_tiled(const Problem &p, Launch *l) {
-    const TileCfg c = kCfg0;
-    const int64_t tm = (p.M + c.bm - 1) / c.bm, tn = (p.N + c.bn - 1) / c.bn;
+    int v = l->variant;  // forced configuration + 1, or 0 for automatic
+    int best;
+    if (v > 0) {
+        if (v > kNumCfgs) return false;
+        best = v - 1;
+    } else {
+        best = 0;
+        double best_cost = cfg_cost(kCfgs[0], p);
+        for (int i = 1; i < kNumCfgs; ++i) {
+            const double c = cfg_cost(kCfgs[i], p);
+            if (c < best_cost) {
+                best = i;
+                best_cost = c;
+            }
+        }
+    }
+    const TileCfg &c = kCfgs[best];
+    const int64_t tm = (p.M + c.bm() - 1) / c.bm(), tn = (p.N + c.bn() - 1) / c.bn();
     l->kernel = OUTPROD_KERNEL_TILED;
-    l->variant = 0;
-    l->tile_m = c.bm;
-    l->tile_n = c.bn;
+    l->variant = best;
+    l->tile_m = c.bm();
+    l->tile_n = c.bn();
     l->tile_k = c.bk;
-    l->block = 64 * c.wgm * c.wgn;
-    l->lds_bytes = 2 * c.bk * ((c.bm + 32) + (c.bn + 32)) * 4;
+    l->block = c.threads();
+    l->lds_bytes = 2 * c.bk * (lds_ld(c.bm(), c.mf) + lds_ld(c.bn(), c.mf)) * 4;
     l->grid = tm * tn * p.ne12 * p.ne13;
     return true;
 }

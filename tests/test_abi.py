@@ -133,7 +133,7 @@ def test_range_limit():
 def test_kernel_choice_on_workloads():
     want = {
         "lora_r8_single": "skinny", "lora_r4_2560": "skinny", "lora_r24_9216": "skinny",
-        "deltanet_bcast": "tiled", "q8_0_5120": "tiled", "q4_K_5120x17408": "tiled",
+        "deltanet_bcast": "skinny", "q8_0_5120": "tiled", "q4_K_5120x17408": "tiled",
         "q4_K_17408x5120": "tiled",
     }
     for name, kern in want.items():
@@ -150,5 +150,12 @@ def test_forced_kernels():
     ne, nb = base(synth.Q8_0, a_ne=(64, 512, 1, 1))
     assert B.STATUS[plan(synth.Q8_0, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
     ne, nb = base(a_ne=(33, 512, 1, 1))
-    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
+    p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_SKINNY)
+    assert p["kernel_name"] == "skinny" and p["tile_m"] == 32 and p["grid"] == 2 * 160
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=7)] == "E_KERNEL"
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 0))] == "E_KERNEL"
+    # every tiled configuration can be forced; an unknown one is refused
+    for cfg in range(10):
+        p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
+        assert p["kernel_name"] == "tiled" and p["variant"] == cfg
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, 40))] == "E_KERNEL"

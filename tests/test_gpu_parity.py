@@ -82,6 +82,18 @@ def test_small_ragged(a_type, a_ne, b_ne, kernel):
     check_case(inst, kernel)
 
 
+@pytest.mark.parametrize("cfg", range(10))
+def test_every_tiled_configuration(cfg):
+    """Each tiled configuration, forced, on ragged shapes of every a type
+    (partial tiles in i0, i1 and K, broadcast slices)."""
+    code = B.kernel_code(B.KERNEL_TILED, cfg)
+    for a_type, a_ne, b_ne in ((synth.F32, (300, 45, 2, 1), (290, 45, 4, 1)),
+                               (synth.Q8_0, (352, 70, 1, 1), (150, 70, 1, 1)),
+                               (synth.Q4_K, (768, 37, 1, 2), (141, 37, 1, 2))):
+        inst = synth.make_instance("cfg%d" % cfg, a_type, a_ne, b_ne, seed_of(cfg, a_type))
+        check_case(inst, code)
+
+
 def test_rank1_K1_bit_exact():
     """K = 1: dst = RN32(a[i0]*b[i1]) exactly, on both kernels."""
     for kernel, ne00 in ((B.KERNEL_SKINNY, 8), (B.KERNEL_TILED, 8), (B.KERNEL_TILED, 200)):
