@@ -7,9 +7,10 @@ every launch of the workload (the default workload, the 27B q4_K weight x f32
 gradient products in both orientations, is two launches: m5120 k17408 n1024
 and m17408 k5120 n1024).  Inputs are resident in HBM before timing starts;
 R copies of them rotate so that consecutive steps do not hit the 256 MB
-Infinity Cache.  Timing: HIP events on the stream the kernels are launched on
-(torch's current stream), W untimed warmup steps, then exactly K timed steps
-between two synchronizations.
+Infinity Cache.  Timing: W untimed warmup steps; K eager steps (reported as
+ms_per_step_eager, host submission included); then exactly K steps captured
+in one HIP graph and replayed between two synchronizations, timed with HIP
+events on the stream the kernels run on.
 
 Prints ONE JSON line (progress goes to stderr).  ``value`` is GFLOP/s of the
 whole step; ``roofline`` reports the dominant kernel's algorithmic rate per
@@ -132,46 +133,64 @@ def main():
     log("rotating sets", R, "set MB %.1f" % (set_bytes / 1e6),
         "plans", [(p[3]["kernel_name"], p[3]["tile_m"], p[3]["tile_n"], p[3]["grid"]) for p in sets[0]])
 
-    def launch(r, j):
+    def launch(r, j, stream_ptr):
         inst = insts[j]
         a_d, b_d, d_d, _ = sets[r][j]
-        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb, sptr)
+        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb,
+                   stream_ptr)
 
     for s in range(args.warmup):
         for j in range(len(insts)):
-            launch(s % R, j)
+            launch(s % R, j, sptr)
     torch.cuda.synchronize()
 
+    # Eager launches, one event pair per step (host submission included).
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in insts] for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for s in range(K):
+        ev[s][0].record(stream)
+        for j in range(len(insts)):
+            launch(s % R, j, sptr)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms_eager = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    # Timed region: exactly K steps captured in one HIP graph (the library's
+    # launches are recorded on the capturing stream), so small kernels are
+    # not limited by host submission.  One untimed replay uploads the graph.
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        cptr = torch.cuda.current_stream(dev).cuda_stream
+        for s in range(K):
+            for j in range(len(insts)):
+                launch(s % R, j, cptr)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for s in range(K):
-        for j in range(len(insts)):
-            ev[s][j][0].record(stream)
-            launch(s % R, j)
-            ev[s][j][1].record(stream)
+    graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / K
-    per_launch = np.array([[ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(insts))]
-                           for s in range(K)])  # ms
-    log("timed %d steps: %.4f ms/step (host wall %.3f s)" % (K, ms_step, wall))
+    log("timed %d steps (graph): %.4f ms/step; eager %.4f ms/step (host wall %.3f s)"
+        % (K, ms_step, ms_eager, wall))
 
-    # dominant kernel: all launches of a workload run one kernel family
-    avg_ms = per_launch.mean(axis=0)
+    # dominant kernel: all launches of a workload run one kernel family; its
+    # average launch duration is the graph's time per launch
     flops_launch = np.array([w[0] for w in work], dtype=np.float64)
     bytes_launch = np.array([w[1] for w in work], dtype=np.float64)
     ai = flops_step / bytes_step
     bound = "mfma" if ai >= RIDGE else "hbm"
     kernels = sorted(set(p[3]["kernel_name"] for p in sets[0]))
     # algorithmic work per launch / the kernel's average launch duration
-    mean_s = float(per_launch.mean()) * 1e-3
+    mean_s = ms_step / len(insts) * 1e-3
     if bound == "mfma":
         achieved = float(flops_launch.mean()) / mean_s / 1e12
         peak, unit = PEAK_MFMA_F32_TFLOPS, "TFLOP/s"
@@ -187,8 +206,7 @@ def main():
         "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
         "frac": round(achieved / peak, 4), "traffic": traffic,
         "kernel": kernels[0] if len(kernels) == 1 else kernels,
-        "avg_launch_us": round(mean_s * 1e6, 2),
-        "avg_launch_us_by_launch": [round(float(x) * 1e3, 2) for x in avg_ms],
+        "avg_launch_us": round(mean_s * 1e6, 3),
         "algorithmic_flops_per_launch": [int(x) for x in flops_launch],
         "algorithmic_bytes_per_launch": [int(x) for x in bytes_launch],
     }
@@ -217,6 +235,7 @@ def main():
             "rotating_input_sets": R,
         },
         "gbps": round(gbps, 1),
+        "ms_per_step_eager": round(ms_eager, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": src_hash,

@@ -130,7 +130,7 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
  * family: (index + 1) << 8, with the index as reported in
  * outprod_plan.variant; 0 lets the library choose.  A family or
  * configuration that cannot run the problem returns OUTPROD_E_KERNEL (e.g.
- * SKINNY for a quantized a, or a configuration index with SKINNY).
+ * SKINNY for a quantized a, or an unknown configuration index).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);

@@ -162,7 +162,8 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     // kernel = family | (tile configuration + 1) << 8; configuration 0 = automatic
     const int variant = (kernel >> 8) & 0xFF;
     kernel &= 0xFF;
-    if (variant != 0 && kernel != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
+    if (variant != 0 && kernel != OUTPROD_KERNEL_TILED && kernel != OUTPROD_KERNEL_SKINNY)
+        return OUTPROD_E_KERNEL;
     l.variant = variant;
     bool ok;
     switch (kernel) {

@@ -46,12 +46,15 @@ struct SliceBase {
 };
 
 __device__ __forceinline__ SliceBase slice_base(const Problem &p, int z) {
-    const int64_t i2 = z % p.ne12, i3 = z / p.ne12;
-    const int64_t i02 = i2 / p.dps2, i03 = i3 / p.dps3;
+    // 32-bit index math (the host guarantees slice counts below 2^31); 64-bit
+    // division would expand into long instruction sequences.
+    const int ne12 = (int)p.ne12, dps2 = (int)p.dps2, dps3 = (int)p.dps3;
+    const int i2 = z % ne12, i3 = z / ne12;
+    const int i02 = i2 / dps2, i03 = i3 / dps3;
     SliceBase s;
-    s.a = p.a + i02 * p.nb02 + i03 * p.nb03;
-    s.b = p.b + i2 * p.nb12 + i3 * p.nb13;
-    s.dst = p.dst + i2 * p.nb2 + i3 * p.nb3;
+    s.a = p.a + (int64_t)i02 * p.nb02 + (int64_t)i03 * p.nb03;
+    s.b = p.b + (int64_t)i2 * p.nb12 + (int64_t)i3 * p.nb13;
+    s.dst = p.dst + (int64_t)i2 * p.nb2 + (int64_t)i3 * p.nb3;
     return s;
 }
 

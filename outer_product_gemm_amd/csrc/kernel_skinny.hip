@@ -23,9 +23,10 @@ namespace outprod {
 namespace {
 
 constexpr int kSkinnyCols = 16;  // columns i1 per workgroup
-constexpr int kUnroll = 8;       // 4-row steps whose loads are issued together
 
-template <int MT, int W>
+// MT: 16-column blocks of a per workgroup; W: waves; U: 4-row steps per wave
+// whose loads are issued together.
+template <int MT, int W, int U>
 __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks, int m_blocks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -55,11 +56,11 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
     for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int steps = (K + 3) / 4;
-    for (int base = wave; base < steps; base += W * kUnroll) {
-        float bv[kUnroll];
-        float av[kUnroll][MT];
+    for (int base = wave; base < steps; base += W * U) {
+        float bv[U];
+        float av[U][MT];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int k = (base + u * W) * 4 + kk;
             const bool kok = k < K;
             bv[u] = (kok && col_ok) ? ldf(bcol + (int64_t)k * p.nb11) : 0.f;
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
                 av[u][t] = (kok && a_ok[t]) ? ldf(acol[t] + (int64_t)k * p.nb01) : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u], av[u][t], acc[t], 0, 0, 0);
@@ -93,22 +94,50 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
     }
 }
 
-constexpr int kSkinnyWaves = 8;
+struct ColCfg {
+    int waves, unroll;
+};
+// 0: 8 waves x 8 steps; 1: 16 x 8; 2: 4 x 16; 3: 16 x 4; 4: 8 x 16
+constexpr ColCfg kColCfgs[] = {{8, 8}, {16, 8}, {4, 16}, {16, 4}, {8, 16}};
+constexpr int kNumColCfgs = sizeof(kColCfgs) / sizeof(kColCfgs[0]);
+
+template <int MT, int C>
+const void *col_fn() {
+    return (const void *)&skinny_kernel<MT, kColCfgs[C].waves, kColCfgs[C].unroll>;
+}
+
+template <int MT>
+const void *col_fn(int c) {
+    switch (c) {
+    case 1: return col_fn<MT, 1>();
+    case 2: return col_fn<MT, 2>();
+    case 3: return col_fn<MT, 3>();
+    case 4: return col_fn<MT, 4>();
+    default: return col_fn<MT, 0>();
+    }
+}
 
 }  // namespace
 
+// l->variant on entry: forced configuration + 1, or 0 for automatic.  On
+// return: the configuration index (the i0 block width is tile_m).
 bool plan_skinny(const Problem &p, Launch *l) {
     if (p.a_type != OUTPROD_TYPE_F32 || p.M < 1) return false;
+    int cfg = 0;
+    if (l->variant > 0) {
+        if (l->variant > kNumColCfgs) return false;
+        cfg = l->variant - 1;
+    }
     const int64_t col_blocks = (p.N + kSkinnyCols - 1) / kSkinnyCols;
     const int mt = p.M > 16 ? 2 : 1;
     const int64_t m_blocks = (p.M + 16 * mt - 1) / (16 * mt);
     l->kernel = OUTPROD_KERNEL_SKINNY;
-    l->variant = mt;
+    l->variant = cfg;
     l->tile_m = 16 * mt;
     l->tile_n = kSkinnyCols;
     l->tile_k = 4;
-    l->block = 64 * kSkinnyWaves;
-    l->lds_bytes = kSkinnyWaves * mt * 256 * 4;
+    l->block = 64 * kColCfgs[cfg].waves;
+    l->lds_bytes = kColCfgs[cfg].waves * mt * 256 * 4;
     l->grid = col_blocks * m_blocks * p.ne12 * p.ne13;
     return true;
 }
@@ -118,8 +147,7 @@ hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s) {
     int m_blocks = (int)((p.M + l.tile_m - 1) / l.tile_m);
     Problem pp = p;
     void *args[] = {&pp, &col_blocks, &m_blocks};
-    const void *fn = l.variant == 2 ? (const void *)&skinny_kernel<2, kSkinnyWaves>
-                                    : (const void *)&skinny_kernel<1, kSkinnyWaves>;
+    const void *fn = l.tile_m == 32 ? col_fn<2>(l.variant) : col_fn<1>(l.variant);
     return hipLaunchKernel(fn, dim3((unsigned)l.grid), dim3(l.block), args, 0, s);
 }
 

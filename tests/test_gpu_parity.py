@@ -94,6 +94,17 @@ def test_every_tiled_configuration(cfg):
         check_case(inst, code)
 
 
+@pytest.mark.parametrize("cfg", range(5))
+def test_every_column_configuration(cfg):
+    """Each column-kernel configuration, forced, on ragged f32 shapes (partial
+    column blocks, i0 blocks, K not a multiple of the wave steps)."""
+    code = B.kernel_code(B.KERNEL_SKINNY, cfg)
+    for a_ne, b_ne in (((8, 517, 1, 1), (333, 517, 1, 1)), ((24, 130, 2, 1), (70, 130, 4, 1)),
+                       ((50, 77, 1, 1), (45, 77, 1, 1))):
+        inst = synth.make_instance("col%d" % cfg, synth.F32, a_ne, b_ne, seed_of(cfg, a_ne))
+        check_case(inst, code)
+
+
 def test_rank1_K1_bit_exact():
     """K = 1: dst = RN32(a[i0]*b[i1]) exactly, on both kernels."""
     for kernel, ne00 in ((B.KERNEL_SKINNY, 8), (B.KERNEL_TILED, 8), (B.KERNEL_TILED, 200)):
@@ -278,3 +289,36 @@ def test_tensor_helper_matches_raw_call():
     torch.cuda.synchronize()
     raw = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
     assert np.array_equal(out.cpu().numpy(), raw)
+
+
+def test_graph_capture_replays_match_eager():
+    """Launches captured in a HIP graph: every replay, with eager work on the
+    same buffers between replays, equals the eager result (b scaled by 2 in
+    place between replays scales dst by exactly 2)."""
+    for name in ("lora_r8_single", "deltanet_bcast", "q8_0_5120"):
+        inst = synth.workload(name)
+        a_d = G.to_dev(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1))
+        b_d = G.to_dev(inst.b)
+        eager = torch.empty(inst.dst_shape, dtype=torch.float32, device="cuda:0")
+        out = torch.empty_like(eager)
+        stream = torch.cuda.current_stream().cuda_stream
+        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), eager.data_ptr(), inst.ne, inst.nb, stream)
+        torch.cuda.synchronize()
+        ref = eager.cpu().numpy()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=cap):
+            B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        scale = 1.0
+        for rep in range(4):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            assert np.array_equal(got, ref * np.float32(scale)), (name, rep)
+            b_d.mul_(2.0)          # eager work on the captured buffer
+            scale *= 2.0
