@@ -7,103 +7,298 @@
 // how fast the chip fills with loads; the per-head shapes have too few
 // 128 x 128 tiles to occupy 256 CUs.
 //
-// Decomposition: one workgroup per 16 consecutive columns i1 of b (64 bytes of
-// every row k) and 16*MT consecutive columns i0 of a, in one dst slice, all K
-// rows.  Its W waves take interleaved 4-row steps of K.  Each step is one
-// v_mfma_f32_16x16x4_f32 per 16 columns of a, whose A operand is read
-// straight from b (lane l: b[k0 + l/16][n0 + l%16]) and whose B operand is
-// read straight from a (lane l: a[k0 + l/16][m0 + 16t + l%16]); the MFMA
-// performs the k reduction inside the instruction.  The W per-wave partial
-// tiles are then summed in LDS in wave order, so the result is deterministic
-// and every dst element has one writer.  No workspace, no atomics.
+// Decomposition: one workgroup per strip of 16*CW consecutive columns i1 of b
+// (16*CW*4 bytes of every row k) and 16*MT consecutive columns i0 of a, in one
+// dst slice, all K rows.  Lane l reads CW consecutive floats of row
+// k0 + l/16 at column n0 + CW*(l%16) with one vector load, so the 16 lanes of
+// a row read one contiguous segment.  Component c of those CW floats is the A
+// operand of one v_mfma_f32_16x16x4_f32 (lane l: b[k0 + l/16][n0 + CW*(l%16) + c])
+// whose B operand is read straight from a (lane l, block t: a[k0 + l/16][m0 + MT*(l%16) + t],
+// so a lane's MT values are one vector load);
+// the MFMA performs the k reduction inside the instruction, and accumulator set
+// c holds the dst columns n0 + CW*i + c.  The W waves take interleaved 4-row
+// steps of K, each wave issuing the loads of U steps together; their partial
+// tiles are summed in LDS in wave order, so the result is deterministic and
+// every dst element has one writer.  No workspace, no atomics.
 #include "kernel_common.h"
 #include "outprod.h"
 
 namespace outprod {
 namespace {
 
-constexpr int kSkinnyCols = 16;  // columns i1 per workgroup
+template <int CW>
+struct VecF;
+template <>
+struct VecF<2> {
+    typedef float type __attribute__((ext_vector_type(2)));
+};
+template <>
+struct VecF<4> {
+    typedef float type __attribute__((ext_vector_type(4)));
+};
 
-// MT: 16-column blocks of a per workgroup; W: waves; U: 4-row steps per wave
-// whose loads are issued together.
-template <int MT, int W, int U>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks, int m_blocks) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int n0 = (logical % col_blocks) * kSkinnyCols;
-    const int rest = logical / col_blocks;
-    const int m0 = (rest % m_blocks) * 16 * MT;
-    const int z = rest / m_blocks;
-    const SliceBase s = slice_base(p, z);
+// CW consecutive floats of b at column `col` of one row.  FULL: the whole
+// strip is in range and 16-byte aligned, so one vector load; otherwise element
+// loads at clamped (in-range) columns, zeroed past the end of the row.
+template <int CW, bool FULL>
+__device__ __forceinline__ void load_cols(const uint8_t *row, int col, int N, float *out) {
+    if constexpr (FULL && CW > 1) {
+        const typename VecF<CW>::type v = *(const typename VecF<CW>::type *)(row + (int64_t)col * 4);
+#pragma unroll
+        for (int c = 0; c < CW; ++c) out[c] = v[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            const int cc = col + c < N ? col + c : N - 1;
+            const float v = ldf(row + (int64_t)cc * 4);
+            out[c] = col + c < N ? v : 0.f;
+        }
+    }
+}
 
-    const int K = (int)p.K, M = (int)p.M;
-    const int col = n0 + (lane & 15);
+// G consecutive floats of one row of a starting at column i0 (G = 1, 2, 4;
+// i0 a multiple of G).  FULL: a's rows are 16-byte aligned and M is a
+// multiple of G, so a group is either wholly in range or wholly past the end:
+// one vector load at the clamped start min(i0, M-G), with no branch (callers
+// zero out-of-range values).  Otherwise element loads at clamped columns.
+template <int G, bool FULL>
+__device__ __forceinline__ void load_a_group(const uint8_t *row, int i0, int M, float *out) {
+    if constexpr (G > 1 && FULL) {
+        const int ic = i0 < M - G ? i0 : M - G;
+        const typename VecF<G>::type v = *(const typename VecF<G>::type *)(row + (int64_t)ic * 4);
+#pragma unroll
+        for (int t = 0; t < G; ++t) out[t] = v[t];
+    } else {
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            const int ii = i0 + t < M ? i0 + t : M - 1;
+            out[t] = ldf(row + (int64_t)ii * 4);
+        }
+    }
+}
+
+// The K loop of one wave.  Loads are unconditional (addresses clamped into
+// range, out-of-range values replaced by zero afterwards) so that the U steps'
+// loads are all in flight before the first MFMA waits on them.
+template <int MT, int CW, int W, int U, bool FULL>
+__device__ __forceinline__ void column_k_loop(const Problem &p, const SliceBase &s, int n0, int m0,
+                                              int wave, int lane, floatx4 (&acc)[CW][MT]) {
+    const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
+    const int col = n0 + CW * (lane & 15);
     const int kk = lane >> 4;
-    const bool col_ok = col < p.N;
-    const uint8_t *bcol = s.b + (int64_t)col * 4;
-    const uint8_t *acol[MT];
+    // the MT values of a this lane supplies are consecutive: i0 = m0 + MT*(l%16) + t
+    const int ia = m0 + MT * (lane & 15);
     bool a_ok[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int i0 = m0 + 16 * t + (lane & 15);
-        a_ok[t] = i0 < M;
-        acol[t] = s.a + (int64_t)i0 * 4;
-    }
-
-    floatx4 acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
+    for (int t = 0; t < MT; ++t) a_ok[t] = ia + t < M;
     const int steps = (K + 3) / 4;
     for (int base = wave; base < steps; base += W * U) {
-        float bv[U];
+        float bv[U][CW];
         float av[U][MT];
+        // a first: its rows are few and cached, so they arrive before b's
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = (base + u * W) * 4 + kk;
-            const bool kok = k < K;
-            bv[u] = (kok && col_ok) ? ldf(bcol + (int64_t)k * p.nb11) : 0.f;
+            const int kc = k < K ? k : K - 1;
+            load_a_group<MT, FULL>(s.a + (int64_t)kc * p.nb01, ia, M, av[u]);
+        }
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                av[u][t] = (kok && a_ok[t]) ? ldf(acol[t] + (int64_t)k * p.nb01) : 0.f;
+        for (int u = 0; u < U; ++u) {
+            const int k = (base + u * W) * 4 + kk;
+            const int kc = k < K ? k : K - 1;
+            load_cols<CW, FULL>(s.b + (int64_t)kc * p.nb11, col, N, bv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kok = (base + u * W) * 4 + kk < K;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) bv[u][c] = kok ? bv[u][c] : 0.f;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) av[u][t] = (kok && a_ok[t]) ? av[u][t] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u], av[u][t], acc[t], 0, 0, 0);
+            for (int c = 0; c < CW; ++c)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u][c], av[u][t], acc[c][t], 0, 0, 0);
     }
+}
 
-    // Sum the W partial tiles in wave order.  Lane l of a wave holds rows
-    // 4*(l/16) + r (columns i1) and column l%16 (i0 within block t).
-    __shared__ float red[W][MT][4][64];
+// MT: 16-column blocks of a; CW: columns of b per lane; W: waves; U: 4-row
+// steps per wave whose loads are issued together.
+template <int MT, int CW, int W, int U>
+__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks, int m_blocks) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int n0 = (logical % col_blocks) * (16 * CW);
+    const int rest = logical / col_blocks;
+    const int m0 = (rest % m_blocks) * 16 * MT;
+    const int z = rest / m_blocks;
+    const SliceBase s = slice_base(p, z);
+    const int M = (int)p.M, N = (int)p.N;
+
+    floatx4 acc[CW][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int c = 0; c < CW; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
+        for (int t = 0; t < MT; ++t) acc[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // whole b strip in range, 16-byte aligned rows of a and b (host-checked)
+    // and M a multiple of the a group: vector loads without branches
+    if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % MT == 0)
+        column_k_loop<MT, CW, W, U, true>(p, s, n0, m0, wave, lane, acc);
+    else
+        column_k_loop<MT, CW, W, U, false>(p, s, n0, m0, wave, lane, acc);
+
+    // Sum the W partial tiles in wave order.  In accumulator set (c, t), lane l
+    // holds rows i = 4*(l/16) + r (dst column i1 = n0 + CW*i + c) and column
+    // j = l%16 (i0 = m0 + MT*j + t).
+    __shared__ float red[W][CW][MT][4][64];
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][c][t][r][lane] = acc[c][t][r];
     __syncthreads();
-    for (int o = threadIdx.x; o < 256 * MT; o += 64 * W) {
-        const int t = o >> 8, r = (o >> 6) & 3, l = o & 63;
+    for (int o = threadIdx.x; o < 256 * CW * MT; o += 64 * W) {
+        const int l = o & 63, r = (o >> 6) & 3, ct = o >> 8;
+        const int t = ct % MT, c = ct / MT;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) sum += red[w][t][r][l];
-        const int i1 = n0 + 4 * (l >> 4) + r;
-        const int i0 = m0 + 16 * t + (l & 15);
-        if (i1 < p.N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
+        for (int w = 0; w < W; ++w) sum += red[w][c][t][r][l];
+        const int i1 = n0 + CW * (4 * (l >> 4) + r) + c;
+        const int i0 = m0 + MT * (l & 15) + t;
+        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
+    }
+}
+
+// ---------------------------------------------------------------- narrow a
+// For ne00 <= 32 the 16-block v_mfma_f32_4x4x1_f32 wastes less than a
+// 16x16x4 padded to 16 columns of a.  Its lanes 4q'..4q'+3 form block q':
+// lane 4q'+i supplies row i of the block's A and column i of its B, and
+// accumulator register r of lane 4q'+j holds D[r][j].  With the same b loads
+// as above (lane l: row k0 + l/16, columns n0 + CW*(l%16) + c), block
+// q' = l/4 covers row k0 + q'/4 and the four b columns n0 + CW*(4*(q'%4) + i) + c;
+// in instruction t its B operand is a[k0 + l/16][m0 + T4*(l%4) + t].  So one instruction per
+// component c and per 4 columns of a adds a 4 x 4 outer product for each of
+// the 4 rows, and the four blocks that share a column group (lanes l, l+16,
+// l+32, l+48) hold partial sums over interleaved rows; they are summed with
+// the waves in the LDS reduction.
+template <int T4, int CW, int W, int U, bool FULL>
+__device__ __forceinline__ void narrow_k_loop(const Problem &p, const SliceBase &s, int n0, int m0,
+                                              int wave, int lane, floatx4 (&acc)[CW][T4]) {
+    const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
+    const int col = n0 + CW * (lane & 15);
+    const int kk = lane >> 4;
+    // the T4 values of a this lane supplies are consecutive: i0 = m0 + T4*(l%4) + t
+    const int ia = m0 + T4 * (lane & 3);
+    bool a_ok[T4];
+#pragma unroll
+    for (int t = 0; t < T4; ++t) a_ok[t] = ia + t < M;
+    const int steps = (K + 3) / 4;
+    for (int base = wave; base < steps; base += W * U) {
+        float bv[U][CW];
+        float av[U][T4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (base + u * W) * 4 + kk;
+            const int kc = k < K ? k : K - 1;
+            load_a_group<T4, FULL>(s.a + (int64_t)kc * p.nb01, ia, M, av[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (base + u * W) * 4 + kk;
+            const int kc = k < K ? k : K - 1;
+            load_cols<CW, FULL>(s.b + (int64_t)kc * p.nb11, col, N, bv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kok = (base + u * W) * 4 + kk < K;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) bv[u][c] = kok ? bv[u][c] : 0.f;
+#pragma unroll
+            for (int t = 0; t < T4; ++t) av[u][t] = (kok && a_ok[t]) ? av[u][t] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+#pragma unroll
+                for (int t = 0; t < T4; ++t)
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(bv[u][c], av[u][t], acc[c][t], 0, 0, 0);
+    }
+}
+
+// T4: 4-column blocks of a (4*T4 columns per workgroup); CW, W, U as above.
+template <int T4, int CW, int W, int U>
+__global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p, int col_blocks, int m_blocks) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int n0 = (logical % col_blocks) * (16 * CW);
+    const int rest = logical / col_blocks;
+    const int m0 = (rest % m_blocks) * 4 * T4;
+    const int z = rest / m_blocks;
+    const SliceBase s = slice_base(p, z);
+    const int M = (int)p.M, N = (int)p.N;
+
+    floatx4 acc[CW][T4];
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int t = 0; t < T4; ++t) acc[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % T4 == 0)
+        narrow_k_loop<T4, CW, W, U, true>(p, s, n0, m0, wave, lane, acc);
+    else
+        narrow_k_loop<T4, CW, W, U, false>(p, s, n0, m0, wave, lane, acc);
+
+    // Register r of lane l in set (c, t): dst column i1 = n0 + CW*(4*((l/4)%4) + r) + c,
+    // i0 = m0 + T4*(l%4) + t, partial over rows k = l/16 (mod 4) of this wave.
+    // Sum over the W waves and the 4 lane groups l/16, in that fixed order.
+    __shared__ float red[W][CW][T4][4][64];
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int t = 0; t < T4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][c][t][r][lane] = acc[c][t][r];
+    __syncthreads();
+    // outputs: (c, t, r, l16) with l16 = lane % 16 -> 64 * CW * T4 of them
+    for (int o = threadIdx.x; o < 64 * CW * T4; o += 64 * W) {
+        const int l16 = o & 15, r = (o >> 4) & 3, ct = o >> 6;
+        const int t = ct % T4, c = ct / T4;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) sum += red[w][c][t][r][l16 + 16 * g];
+        const int i1 = n0 + CW * (4 * (l16 >> 2) + r) + c;
+        const int i0 = m0 + T4 * (l16 & 3) + t;
+        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
     }
 }
 
 struct ColCfg {
-    int waves, unroll;
+    int mma, cw, waves, unroll;  // mma: 16 = 16x16x4 kernel, 4 = 4x4x1 kernel
 };
-// 0: 8 waves x 8 steps; 1: 16 x 8; 2: 4 x 16; 3: 16 x 4; 4: 8 x 16
-constexpr ColCfg kColCfgs[] = {{8, 8}, {16, 8}, {4, 16}, {16, 4}, {8, 16}};
+// 16x16x4: 0: 16-col strips, 8 waves x 8 steps   1: 32-col, 8 x 8   2: 64-col, 8 x 8
+//          3: 32-col, 16 x 8   4: 64-col, 8 x 16   5: 16-col, 16 x 8
+// 4x4x1:   6: 16-col, 8 x 16   7: 32-col, 8 x 16   8: 64-col, 8 x 16
+//          9: 32-col, 8 x 8    10: 64-col, 8 x 8
+constexpr ColCfg kColCfgs[] = {{16, 1, 8, 8}, {16, 2, 8, 8},  {16, 4, 8, 8}, {16, 2, 16, 8},
+                               {16, 4, 8, 16}, {16, 1, 16, 8}, {4, 1, 8, 16}, {4, 2, 8, 16},
+                               {4, 4, 8, 16},  {4, 2, 8, 8},   {4, 4, 8, 8}};
 constexpr int kNumColCfgs = sizeof(kColCfgs) / sizeof(kColCfgs[0]);
 
 template <int MT, int C>
 const void *col_fn() {
-    return (const void *)&skinny_kernel<MT, kColCfgs[C].waves, kColCfgs[C].unroll>;
+    constexpr ColCfg c = kColCfgs[C];
+    return (const void *)&skinny_kernel<MT, c.cw, c.waves, c.unroll>;
 }
 
 template <int MT>
@@ -113,7 +308,37 @@ const void *col_fn(int c) {
     case 2: return col_fn<MT, 2>();
     case 3: return col_fn<MT, 3>();
     case 4: return col_fn<MT, 4>();
+    case 5: return col_fn<MT, 5>();
     default: return col_fn<MT, 0>();
+    }
+}
+
+template <int T4, int C>
+const void *narrow_fn() {
+    constexpr ColCfg c = kColCfgs[C];
+    return (const void *)&narrow_kernel<T4, c.cw, c.waves, c.unroll>;
+}
+
+template <int T4>
+const void *narrow_fn(int c) {
+    switch (c) {
+    case 7: return narrow_fn<T4, 7>();
+    case 8: return narrow_fn<T4, 8>();
+    case 9: return narrow_fn<T4, 9>();
+    case 10: return narrow_fn<T4, 10>();
+    default: return narrow_fn<T4, 6>();
+    }
+}
+
+// 4-column blocks of a per workgroup for the narrow kernel (at most 16
+// columns of a; wider a takes several i0 blocks)
+int narrow_t4(int64_t M) { return M <= 4 ? 1 : M <= 8 ? 2 : 4; }
+
+const void *narrow_dispatch(int t4, int c) {
+    switch (t4) {
+    case 1: return narrow_fn<1>(c);
+    case 2: return narrow_fn<2>(c);
+    default: return narrow_fn<4>(c);
     }
 }
 
@@ -123,31 +348,53 @@ const void *col_fn(int c) {
 // return: the configuration index (the i0 block width is tile_m).
 bool plan_skinny(const Problem &p, Launch *l) {
     if (p.a_type != OUTPROD_TYPE_F32 || p.M < 1) return false;
-    int cfg = 0;
+    int cfg;
     if (l->variant > 0) {
         if (l->variant > kNumColCfgs) return false;
         cfg = l->variant - 1;
+    } else {
+        // measured on MI355X with HBM-resident (cache-cold) inputs, K = 512:
+        // ranks <= 8 over wide b read 256-byte row segments with the 4x4x1
+        // MFMA; narrower b needs more workgroups (16-column strips); wider a
+        // uses the 16x16x4 kernel
+        if (p.M <= 4)
+            cfg = p.N >= 4096 ? 10 : 6;
+        else if (p.M <= 8)
+            cfg = p.N >= 4096 ? 10 : 0;
+        else
+            cfg = 0;
     }
-    const int64_t col_blocks = (p.N + kSkinnyCols - 1) / kSkinnyCols;
-    const int mt = p.M > 16 ? 2 : 1;
-    const int64_t m_blocks = (p.M + 16 * mt - 1) / (16 * mt);
+    const ColCfg &c = kColCfgs[cfg];
+    const int cols = 16 * c.cw;
+    const int64_t col_blocks = (p.N + cols - 1) / cols;
+    int tile_m;
+    if (c.mma == 4) {
+        tile_m = 4 * narrow_t4(p.M);
+    } else {
+        tile_m = p.M > 16 ? 32 : 16;
+    }
+    const int64_t m_blocks = (p.M + tile_m - 1) / tile_m;
     l->kernel = OUTPROD_KERNEL_SKINNY;
     l->variant = cfg;
-    l->tile_m = 16 * mt;
-    l->tile_n = kSkinnyCols;
+    l->tile_m = tile_m;
+    l->tile_n = cols;
     l->tile_k = 4;
-    l->block = 64 * kColCfgs[cfg].waves;
-    l->lds_bytes = kColCfgs[cfg].waves * mt * 256 * 4;
+    l->block = 64 * c.waves;
+    l->lds_bytes = c.waves * c.cw * (c.mma == 4 ? tile_m / 4 : tile_m / 16) * 256 * 4;
     l->grid = col_blocks * m_blocks * p.ne12 * p.ne13;
     return true;
 }
 
 hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s) {
-    int col_blocks = (int)((p.N + kSkinnyCols - 1) / kSkinnyCols);
+    int col_blocks = (int)((p.N + l.tile_n - 1) / l.tile_n);
     int m_blocks = (int)((p.M + l.tile_m - 1) / l.tile_m);
     Problem pp = p;
     void *args[] = {&pp, &col_blocks, &m_blocks};
-    const void *fn = l.tile_m == 32 ? col_fn<2>(l.variant) : col_fn<1>(l.variant);
+    const void *fn;
+    if (kColCfgs[l.variant].mma == 4)
+        fn = narrow_dispatch(l.tile_m / 4, l.variant);
+    else
+        fn = l.tile_m == 32 ? col_fn<2>(l.variant) : col_fn<1>(l.variant);
     return hipLaunchKernel(fn, dim3((unsigned)l.grid), dim3(l.block), args, 0, s);
 }
 

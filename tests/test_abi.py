@@ -153,10 +153,10 @@ def test_forced_kernels():
     p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_SKINNY)
     assert p["kernel_name"] == "skinny" and p["tile_m"] == 32 and p["grid"] == 2 * 160
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=7)] == "E_KERNEL"
-    for cfg in range(5):
+    for cfg in range(11):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_SKINNY, cfg))
         assert p["kernel_name"] == "skinny" and p["variant"] == cfg
-    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 5))] == "E_KERNEL"
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 11))] == "E_KERNEL"
     # every tiled configuration can be forced; an unknown one is refused
     for cfg in range(10):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
