@@ -53,7 +53,12 @@ PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0}
 # HBM traffic per launch from rocprofv3 PMC runs (FETCH_SIZE + WRITE_SIZE,
 # scaled by the copy-kernel calibration), keyed by workload, valid only for
 # the kernel sources whose hash is recorded with it.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # profiles/tiled_q4K_27B_lora_backward.md: launch A 493.5 MB, launch B 523.2 MB
+    "q4_K_27B_both": {"kernel_hash": "14be852d858fe4f1", "bytes_per_launch": 508.37e6},
+    # profiles/column_lora_rank_and_deltanet.md
+    "lora_r8_9216": {"kernel_hash": "14be852d858fe4f1", "bytes_per_launch": 19.40e6},
+}
 
 
 def log(*a):
@@ -92,7 +97,13 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for 600 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU-oracle time for the baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="instead of the benchmark: run a plain device copy of MB megabytes "
+                         "5 times (the reference for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -201,7 +212,7 @@ def main():
     traffic = None
     mt = MEASURED_TRAFFIC.get(args.workload)
     if mt and mt.get("kernel_hash") == src_hash:
-        traffic = mt["bytes_per_launch"]
+        traffic = int(mt["bytes_per_launch"])
     roofline = {
         "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
         "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -244,6 +255,22 @@ def main():
         out["vs_baseline_note"] = ("ratio to the pages' float-staging per-op times for the same "
                                    "shapes on an Apple M5 (Metal): another machine, context only")
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(mb):
+    """A plain device-to-device copy of known size, 5 times: under rocprofv3
+    --pmc its FETCH_SIZE / WRITE_SIZE per dispatch against the known bytes give
+    the factor that scales those counters to HBM bytes."""
+    import torch
+    n = int(mb * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "copies": 5}), flush=True)
 
 
 def cpu_baseline(insts, sets, target_s):
