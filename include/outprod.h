@@ -23,10 +23,14 @@
  *            dst = [ne00, ne10, ne12, ne13]
  *   nb[12] = byte strides in the same order.
  *     nb[0]: 4 for f32 a, else the block size in bytes (34 for q8_0, 144 for
- *            q4_K); nb[4] and nb[8] must be 4 (dim 0 is contiguous).
+ *            q4_K); nb[8] must be 4 (dst dim 0 is contiguous).
+ *     b: either nb[4] == 4 (row-major: each k selects a contiguous row of ne10
+ *            floats) or nb[5] == 4 (K contiguous: a transposed view such as
+ *            the grad^T that the matmul backward passes for the input gradient);
+ *            the other b stride is any multiple of 4.
  *     nb[1..3], nb[5..7], nb[9..11]: any non-negative byte strides (views,
  *            padded rows, stride-0 broadcast of inputs), aligned to 4 bytes
- *            (2 for q8_0 a).  dst's dims must not overlap one another.
+ *            (2 for q8_0 a).  dst's dims must be ordered and must not overlap.
  *
  * Memory and ownership: a, b and dst are DEVICE pointers owned by the caller.
  * The library keeps no pointer after a call returns, allocates nothing and
@@ -110,6 +114,8 @@ typedef struct outprod_plan {
     int64_t dps3;     /* ne13 / ne03 */
     int64_t flops;    /* 2 * ne00 * ne10 * K * slices */
     int variant;      /* configuration index within the family */
+    int swapped;      /* 1: run as the operand-swapped problem (narrow f32 b with a
+                         wide f32 a); tile_m then runs along ne10, tile_n along ne00 */
 } outprod_plan;
 
 /*

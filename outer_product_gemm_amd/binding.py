@@ -58,7 +58,8 @@ class outprod_plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
                 ("tile_k", ctypes.c_int), ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
-                ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int)]
+                ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int),
+                ("swapped", ctypes.c_int)]
 
 
 _I64x12 = ctypes.c_int64 * 12

@@ -52,7 +52,36 @@ bool overlaps(const void *p, int64_t np, const void *q, int64_t nq) {
 struct Checked {
     Problem p;
     Launch l;
+    bool swapped;
 };
+
+// The same OUT_PROD with the roles of a and b exchanged: dst^T = a'·b'^T with
+// a' = b, b' = a, so dst element (i0, i1) is element (i1, i0) of the swapped
+// problem (dst strides exchanged).  Used for a narrow f32 b (ne10 <= 32) with a
+// wide f32 a, e.g. the gradient of a LoRA down-projection out_prod(x, grad_h),
+// so the column kernel can stream the wide operand.  The slice broadcast
+// stays on the original a, which is now the kernel's b.
+Problem swap_operands(const Problem &p) {
+    Problem q = p;
+    q.a = p.b;
+    q.b = p.a;
+    q.M = p.N;
+    q.N = p.M;
+    q.nb01 = p.nb11;
+    q.nb02 = p.nb12;
+    q.nb03 = p.nb13;
+    q.nb10 = 4;
+    q.nb11 = p.nb01;
+    q.nb12 = p.nb02;
+    q.nb13 = p.nb03;
+    q.nb0 = p.nb1;
+    q.nb1 = p.nb0;
+    q.vec_a = p.vec_b;
+    q.vec_b = p.vec_a;
+    q.b_kt = false;
+    q.bcast_b = true;
+    return q;
+}
 
 int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
                       const int64_t *ne, const int64_t *nb, int kernel, Checked *c) {
@@ -93,10 +122,17 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     if (ne00 % block_values(a_type) != 0) return OUTPROD_E_QK;
 
     // strides and alignment
-    if (nb[0] != block_bytes(a_type) || nb[4] != 4 || nb[8] != 4) return OUTPROD_E_LAYOUT;
+    // b is either row-major (dim 0 contiguous, nb10 == 4) or K-contiguous
+    // (nb11 == 4: a transposed view such as the gradient grad^T that the
+    // matmul backward passes for the input gradient); a and dst have dim 0
+    // contiguous.
+    if (nb[0] != block_bytes(a_type) || nb[8] != 4) return OUTPROD_E_LAYOUT;
     for (int i = 0; i < 12; ++i)
         if (nb[i] < 0) return OUTPROD_E_LAYOUT;
+    const bool b_rows = nb[4] == 4;
+    if (!b_rows && nb[5] != 4) return OUTPROD_E_LAYOUT;
     const int al = align_of(a_type);
+    if (nb[4] % 4 != 0) return OUTPROD_E_LAYOUT;
     for (int i = 1; i < 4; ++i)
         if (nb[i] % al != 0 || nb[4 + i] % 4 != 0 || nb[8 + i] % 4 != 0) return OUTPROD_E_LAYOUT;
     if ((uintptr_t)a % al != 0 || (uintptr_t)b % 4 != 0 || (uintptr_t)dst % 4 != 0)
@@ -124,8 +160,11 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     int64_t ext_a = 0, ext_b = 0, ext_d = 0;
     if (K > 0) {
         const int64_t ane[4] = {ne00, K, ne02, ne03}, anb[4] = {nb[0], nb[1], nb[2], nb[3]};
-        const int64_t bne[4] = {ne10, K, ne12, ne13}, bnb[4] = {4, nb[5], nb[6], nb[7]};
-        if (!extent(a_row, ane, anb, &ext_a) || !extent(4 * ne10, bne, bnb, &ext_b))
+        // b: last byte = 4 + sum over its four dims of (ne - 1) * nb (either dim
+        // 0 or dim 1 may be the contiguous one)
+        const int64_t bne[4] = {ne10, K, ne12, ne13}, bnb[4] = {nb[4], nb[5], nb[6], nb[7]};
+        if (!extent(a_row, ane, anb, &ext_a) || !mul_add(ne10 - 1, nb[4], 4, &ext_b) ||
+            !extent(ext_b, bne, bnb, &ext_b))
             return OUTPROD_E_RANGE;
     }
     {
@@ -141,7 +180,10 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     p.nb01 = nb[1];
     p.nb02 = nb[2];
     p.nb03 = nb[3];
+    p.nb10 = nb[4];
     p.nb11 = nb[5];
+    p.b_kt = !b_rows;
+    p.nb0 = 4;
     p.nb12 = nb[6];
     p.nb13 = nb[7];
     p.nb1 = nb[9];
@@ -149,7 +191,10 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     p.nb3 = nb[11];
     p.vec_a = a_type == OUTPROD_TYPE_F32 && (uintptr_t)a % 16 == 0 && nb[1] % 16 == 0 &&
               nb[2] % 16 == 0 && nb[3] % 16 == 0;
-    p.vec_b = (uintptr_t)b % 16 == 0 && nb[5] % 16 == 0 && nb[6] % 16 == 0 && nb[7] % 16 == 0;
+    // 16-byte vector loads of b: along its contiguous dim, so the other
+    // strides must keep 16-byte alignment
+    p.vec_b = (uintptr_t)b % 16 == 0 && (b_rows ? nb[5] : nb[4]) % 16 == 0 && nb[6] % 16 == 0 &&
+              nb[7] % 16 == 0;
 
     if (K == 0) {
         const int fam = kernel & 0xFF;
@@ -169,10 +214,19 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     switch (kernel) {
     case OUTPROD_KERNEL_AUTO: {
         // narrow f32 a, or an f32 problem with too few output tiles to fill
-        // the chip: the column kernel; everything else: the tiled kernel
+        // the chip: the column kernel; a narrow row-major b with a wide f32 a:
+        // the column kernel on the operand-swapped problem; everything else:
+        // the tiled kernel
         Launch t = l;
         const bool tiled_ok = plan_tiled(p, &t);
-        if (p.a_type == OUTPROD_TYPE_F32 && (p.M <= 32 || !tiled_ok || t.grid < 128)) {
+        const bool f32 = p.a_type == OUTPROD_TYPE_F32;
+        if (f32 && p.M <= 32) {
+            ok = plan_skinny(p, &l);
+        } else if (f32 && p.N <= 32 && !p.b_kt) {
+            c->p = swap_operands(p);
+            c->swapped = true;
+            ok = plan_skinny(c->p, &l);
+        } else if (f32 && (!tiled_ok || t.grid < 128)) {
             ok = plan_skinny(p, &l);
         } else {
             l = t;
@@ -253,6 +307,7 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
     plan->dps3 = c.p.dps3;
     plan->flops = 2 * c.p.M * c.p.N * c.p.K * plan->slices;
     plan->variant = c.l.variant;
+    plan->swapped = c.swapped ? 1 : 0;
     return OUTPROD_OK;
 }
 

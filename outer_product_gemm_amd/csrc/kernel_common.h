@@ -52,8 +52,13 @@ __device__ __forceinline__ SliceBase slice_base(const Problem &p, int z) {
     const int i2 = z % ne12, i3 = z / ne12;
     const int i02 = i2 / dps2, i03 = i3 / dps3;
     SliceBase s;
-    s.a = p.a + (int64_t)i02 * p.nb02 + (int64_t)i03 * p.nb03;
-    s.b = p.b + (int64_t)i2 * p.nb12 + (int64_t)i3 * p.nb13;
+    if (p.bcast_b) {  // operand-swapped problem: the broadcast side is b
+        s.a = p.a + (int64_t)i2 * p.nb02 + (int64_t)i3 * p.nb03;
+        s.b = p.b + (int64_t)i02 * p.nb12 + (int64_t)i03 * p.nb13;
+    } else {
+        s.a = p.a + (int64_t)i02 * p.nb02 + (int64_t)i03 * p.nb03;
+        s.b = p.b + (int64_t)i2 * p.nb12 + (int64_t)i3 * p.nb13;
+    }
     s.dst = p.dst + (int64_t)i2 * p.nb2 + (int64_t)i3 * p.nb3;
     return s;
 }

@@ -126,6 +126,73 @@ __device__ __forceinline__ void column_k_loop(const Problem &p, const SliceBase 
     }
 }
 
+// b with its K dim contiguous (a transposed view, column stride nb10), CW = 1:
+// lane l reads the 4 consecutive rows kb = k0 + 4*(l/16) .. kb+3 of column
+// n0 + l%16 with one 16-byte load.  Component e is the A operand of MFMA step
+// e, whose rows are kb + e across the four lane groups (an MFMA's k set need
+// not be contiguous; its B operand uses the same rows).  A super-step covers
+// 16 rows; the W waves take interleaved super-steps, U of them per batch.
+template <int MT, int W, int U, bool FULL>
+__device__ __forceinline__ void column_k_loop_kt(const Problem &p, const SliceBase &s, int n0, int m0,
+                                                 int wave, int lane, floatx4 (&acc)[1][MT]) {
+    const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
+    const int col = n0 + (lane & 15);
+    const int kq = lane >> 4;
+    const uint8_t *bcol = s.b + (int64_t)(col < N ? col : N - 1) * p.nb10;
+    const int ia = m0 + MT * (lane & 15);
+    bool a_ok[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_ok[t] = ia + t < M;
+    const int ssteps = (K + 15) / 16;
+    for (int base = wave; base < ssteps; base += W * U) {
+        float bv[U][4];
+        float av[U][4][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kc = kb + e < K ? kb + e : K - 1;
+                load_a_group<MT, FULL>(s.a + (int64_t)kc * p.nb01, ia, M, av[u][e]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+            if constexpr (FULL) {
+                const int kc = kb < K ? kb : K - 4;  // K % 16 == 0 on this path
+                const floatx4 v = *(const floatx4 *)(bcol + (int64_t)kc * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[u][e] = v[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kc = kb + e < K ? kb + e : K - 1;
+                    bv[u][e] = ldf(bcol + (int64_t)kc * 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool kok = kb + e < K;
+                bv[u][e] = (kok && col < N) ? bv[u][e] : 0.f;
+#pragma unroll
+                for (int t = 0; t < MT; ++t) av[u][e][t] = (kok && a_ok[t]) ? av[u][e][t] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u][e], av[u][e][t], acc[0][t], 0, 0, 0);
+    }
+}
+
 // MT: 16-column blocks of a; CW: columns of b per lane; W: waves; U: 4-row
 // steps per wave whose loads are issued together.
 template <int MT, int CW, int W, int U>
@@ -148,10 +215,20 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
 
     // whole b strip in range, 16-byte aligned rows of a and b (host-checked)
     // and M a multiple of the a group: vector loads without branches
-    if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % MT == 0)
+    if (p.b_kt) {
+        // K-contiguous b: CW == 1 configurations only (the planner enforces it);
+        // a super-step is 16 rows, so U/4 of them per batch
+        if constexpr (CW == 1) {
+            if (p.vec_b && p.vec_a && n0 + 16 <= N && M % MT == 0 && p.K % 16 == 0)
+                column_k_loop_kt<MT, W, (U >= 4 ? U / 4 : 1), true>(p, s, n0, m0, wave, lane, acc);
+            else
+                column_k_loop_kt<MT, W, (U >= 4 ? U / 4 : 1), false>(p, s, n0, m0, wave, lane, acc);
+        }
+    } else if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % MT == 0) {
         column_k_loop<MT, CW, W, U, true>(p, s, n0, m0, wave, lane, acc);
-    else
+    } else {
         column_k_loop<MT, CW, W, U, false>(p, s, n0, m0, wave, lane, acc);
+    }
 
     // Sum the W partial tiles in wave order.  In accumulator set (c, t), lane l
     // holds rows i = 4*(l/16) + r (dst column i1 = n0 + CW*i + c) and column
@@ -172,7 +249,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_block
         for (int w = 0; w < W; ++w) sum += red[w][c][t][r][l];
         const int i1 = n0 + CW * (4 * (l >> 4) + r) + c;
         const int i0 = m0 + MT * (l & 15) + t;
-        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
+        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * p.nb0) = sum;
     }
 }
 
@@ -233,6 +310,69 @@ __device__ __forceinline__ void narrow_k_loop(const Problem &p, const SliceBase 
     }
 }
 
+// K-contiguous b for the narrow kernel (CW = 1), with the same 16-row
+// super-steps as column_k_loop_kt.
+template <int T4, int W, int U, bool FULL>
+__device__ __forceinline__ void narrow_k_loop_kt(const Problem &p, const SliceBase &s, int n0, int m0,
+                                                 int wave, int lane, floatx4 (&acc)[1][T4]) {
+    const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
+    const int col = n0 + (lane & 15);
+    const int kq = lane >> 4;
+    const uint8_t *bcol = s.b + (int64_t)(col < N ? col : N - 1) * p.nb10;
+    const int ia = m0 + T4 * (lane & 3);
+    bool a_ok[T4];
+#pragma unroll
+    for (int t = 0; t < T4; ++t) a_ok[t] = ia + t < M;
+    const int ssteps = (K + 15) / 16;
+    for (int base = wave; base < ssteps; base += W * U) {
+        float bv[U][4];
+        float av[U][4][T4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kc = kb + e < K ? kb + e : K - 1;
+                load_a_group<T4, FULL>(s.a + (int64_t)kc * p.nb01, ia, M, av[u][e]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+            if constexpr (FULL) {
+                const int kc = kb < K ? kb : K - 4;
+                const floatx4 v = *(const floatx4 *)(bcol + (int64_t)kc * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[u][e] = v[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kc = kb + e < K ? kb + e : K - 1;
+                    bv[u][e] = ldf(bcol + (int64_t)kc * 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (base + u * W) * 16 + 4 * kq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool kok = kb + e < K;
+                bv[u][e] = (kok && col < N) ? bv[u][e] : 0.f;
+#pragma unroll
+                for (int t = 0; t < T4; ++t) av[u][e][t] = (kok && a_ok[t]) ? av[u][e][t] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int t = 0; t < T4; ++t)
+                    acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(bv[u][e], av[u][e][t], acc[0][t], 0, 0, 0);
+    }
+}
+
 // T4: 4-column blocks of a (4*T4 columns per workgroup); CW, W, U as above.
 template <int T4, int CW, int W, int U>
 __global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p, int col_blocks, int m_blocks) {
@@ -252,10 +392,18 @@ __global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p, int col_block
 #pragma unroll
         for (int t = 0; t < T4; ++t) acc[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % T4 == 0)
+    if (p.b_kt) {
+        if constexpr (CW == 1) {
+            if (p.vec_b && p.vec_a && n0 + 16 <= N && M % T4 == 0 && p.K % 16 == 0)
+                narrow_k_loop_kt<T4, W, (U >= 4 ? U / 4 : 1), true>(p, s, n0, m0, wave, lane, acc);
+            else
+                narrow_k_loop_kt<T4, W, (U >= 4 ? U / 4 : 1), false>(p, s, n0, m0, wave, lane, acc);
+        }
+    } else if (p.vec_b && p.vec_a && n0 + 16 * CW <= N && M % T4 == 0) {
         narrow_k_loop<T4, CW, W, U, true>(p, s, n0, m0, wave, lane, acc);
-    else
+    } else {
         narrow_k_loop<T4, CW, W, U, false>(p, s, n0, m0, wave, lane, acc);
+    }
 
     // Register r of lane l in set (c, t): dst column i1 = n0 + CW*(4*((l/4)%4) + r) + c,
     // i0 = m0 + T4*(l%4) + t, partial over rows k = l/16 (mod 4) of this wave.
@@ -279,7 +427,7 @@ __global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p, int col_block
             for (int g = 0; g < 4; ++g) sum += red[w][c][t][r][l16 + 16 * g];
         const int i1 = n0 + CW * (4 * (l16 >> 2) + r) + c;
         const int i0 = m0 + T4 * (l16 & 3) + t;
-        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = sum;
+        if (i1 < N && i0 < M) *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * p.nb0) = sum;
     }
 }
 
@@ -363,6 +511,10 @@ bool plan_skinny(const Problem &p, Launch *l) {
             cfg = p.N >= 4096 ? 10 : 0;
         else
             cfg = 0;
+    }
+    if (p.b_kt && kColCfgs[cfg].cw != 1) {
+        if (l->variant > 0) return false;  // forced wide-strip configuration
+        cfg = p.M <= 8 ? 6 : 0;            // K-contiguous b: one column per lane
     }
     const ColCfg &c = kColCfgs[cfg];
     const int cols = 16 * c.cw;

@@ -17,9 +17,13 @@
 // through stage t's MFMAs they are decoded into the other LDS buffer and the
 // loads of stage t+2 are issued, so a global load has a whole stage of matrix
 // work to arrive.  One barrier per stage.
+// b may also have its K dim contiguous (the transposed gradient view of the
+// matmul backward); that loader transposes into the same LDS tile.
 // MFMA operand roles: A operand (rows) = b values -> dst rows i1;
 // B operand (columns) = a values -> dst columns i0, so the lanes of one
 // accumulator row write consecutive floats of a dst row.
+#include <type_traits>
+
 #include "kernel_common.h"
 #include "outprod.h"
 
@@ -83,6 +87,64 @@ struct F32Loader {
             if (kGroups % T == 0 || g < kGroups) {
                 const int row = g / (BW / 4), c = 4 * (g % (BW / 4));
                 *(floatx4 *)&lds[row][c] = r[j];
+            }
+        }
+    }
+};
+
+// f32 b whose K dim is contiguous (a transposed view; column stride `ld`):
+// groups of 4 consecutive k of one column, written transposed into the same
+// [k][column] LDS tile.
+template <int BW, int BK, int T>
+struct F32LoaderKT {
+    static constexpr int kGroups = BK / 4 * BW;
+    static constexpr int kPer = (kGroups + T - 1) / T;
+    static_assert(BK % 4 == 0, "stage rows must be a multiple of 4");
+    const uint8_t *base;
+    int64_t ld;
+    int w0, W, K, tid;
+    bool vec;
+    floatx4 r[kPer];
+
+    __device__ void init(const uint8_t *slice, int64_t col_stride, int width, int k_len,
+                         int col0, bool vec_ok, int t) {
+        base = slice;
+        ld = col_stride;
+        W = width;
+        K = k_len;
+        w0 = col0;
+        vec = vec_ok;
+        tid = t;
+    }
+    __device__ void load(int k0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int g = tid + T * j;
+            const int n = g % BW, kq = g / BW;
+            const int c = w0 + n, k = k0 + 4 * kq;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if ((kGroups % T == 0 || g < kGroups) && c < W) {
+                const uint8_t *ptr = base + (int64_t)c * ld + (int64_t)k * 4;
+                if (vec && k + 3 < K) {
+                    v = *(const floatx4 *)ptr;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k + e < K) v[e] = ldf(ptr + 4 * e);
+                }
+            }
+            r[j] = v;
+        }
+    }
+    template <int LD>
+    __device__ void store(float (*lds)[LD]) const {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int g = tid + T * j;
+            if (kGroups % T == 0 || g < kGroups) {
+                const int n = g % BW, kq = g / BW;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lds[4 * kq + e][n] = r[j][e];
             }
         }
     }
@@ -279,7 +341,7 @@ __host__ __device__ constexpr int lds_ld(int bw, int mf) {
 
 // ---------------------------------------------------------------- kernel
 
-template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK>
+template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int tiles_m,
                                                                int tiles_n) {
     typedef Mfma<MF> MM;
@@ -302,9 +364,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int ti
     const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
 
     typename ALoaderFor<AT, BM, BK, T>::type la;
-    F32Loader<BN, BK, T> lb;
+    typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
-    lb.init(s.b, p.nb11, N, K, n0, p.vec_b, tid);
+    lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
 
     typename MM::acc_t acc[FM][FN];
 #pragma unroll
@@ -422,26 +484,31 @@ constexpr TileCfg kCfgs[] = {
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int AT, int C>
+template <int AT, int C, bool BT>
 const void *cfg_fn() {
     constexpr TileCfg c = kCfgs[C];
-    return (const void *)&tiled_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk>;
+    return (const void *)&tiled_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk, BT>;
+}
+
+template <int AT, bool BT>
+const void *tiled_fn(int variant) {
+    switch (variant) {
+    case 1: return cfg_fn<AT, 1, BT>();
+    case 2: return cfg_fn<AT, 2, BT>();
+    case 3: return cfg_fn<AT, 3, BT>();
+    case 4: return cfg_fn<AT, 4, BT>();
+    case 5: return cfg_fn<AT, 5, BT>();
+    case 6: return cfg_fn<AT, 6, BT>();
+    case 7: return cfg_fn<AT, 7, BT>();
+    case 8: return cfg_fn<AT, 8, BT>();
+    case 9: return cfg_fn<AT, 9, BT>();
+    default: return cfg_fn<AT, 0, BT>();
+    }
 }
 
 template <int AT>
-const void *tiled_fn(int variant) {
-    switch (variant) {
-    case 1: return cfg_fn<AT, 1>();
-    case 2: return cfg_fn<AT, 2>();
-    case 3: return cfg_fn<AT, 3>();
-    case 4: return cfg_fn<AT, 4>();
-    case 5: return cfg_fn<AT, 5>();
-    case 6: return cfg_fn<AT, 6>();
-    case 7: return cfg_fn<AT, 7>();
-    case 8: return cfg_fn<AT, 8>();
-    case 9: return cfg_fn<AT, 9>();
-    default: return cfg_fn<AT, 0>();
-    }
+const void *tiled_fn(int variant, bool bt) {
+    return bt ? tiled_fn<AT, true>(variant) : tiled_fn<AT, false>(variant);
 }
 
 // Estimated time of a configuration: the busiest CU runs ceil(tiles / 256)
@@ -491,9 +558,9 @@ hipError_t launch_tiled(const Problem &p, const Launch &l, hipStream_t s) {
     void *args[] = {&pp, &tiles_m, &tiles_n};
     const void *fn;
     switch (p.a_type) {
-    case OUTPROD_TYPE_F32: fn = tiled_fn<OUTPROD_TYPE_F32>(l.variant); break;
-    case OUTPROD_TYPE_Q8_0: fn = tiled_fn<OUTPROD_TYPE_Q8_0>(l.variant); break;
-    case OUTPROD_TYPE_Q4_K: fn = tiled_fn<OUTPROD_TYPE_Q4_K>(l.variant); break;
+    case OUTPROD_TYPE_F32: fn = tiled_fn<OUTPROD_TYPE_F32>(l.variant, p.b_kt); break;
+    case OUTPROD_TYPE_Q8_0: fn = tiled_fn<OUTPROD_TYPE_Q8_0>(l.variant, p.b_kt); break;
+    case OUTPROD_TYPE_Q4_K: fn = tiled_fn<OUTPROD_TYPE_Q4_K>(l.variant, p.b_kt); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, dim3((unsigned)l.grid), dim3(l.block), args, 0, s);

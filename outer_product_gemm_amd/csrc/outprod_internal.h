@@ -18,12 +18,15 @@ struct Problem {
     int64_t N;            // ne10 (b's width, dst dim 1)
     int64_t K;            // contraction length
     int64_t nb01, nb02, nb03;
-    int64_t nb11, nb12, nb13;
-    int64_t nb1, nb2, nb3;  // dst
-    int64_t ne12, ne13;     // dst slices
-    int64_t dps2, dps3;     // broadcast ratios
-    bool vec_a;             // f32 a: base and strides 16-byte aligned
-    bool vec_b;             // b: base and strides 16-byte aligned
+    int64_t nb10, nb11, nb12, nb13;  // b: nb10 == 4 (row-major) or nb11 == 4 (b_kt)
+    int64_t nb0, nb1, nb2, nb3;      // dst: nb0 == 4 except in an operand-swapped problem
+    int64_t ne12, ne13;              // dst slices
+    int64_t dps2, dps3;              // broadcast ratios
+    bool vec_a;    // f32 a: base and strides 16-byte aligned
+    bool vec_b;    // b: base and strides (other than the contiguous one) 16-byte aligned
+    bool b_kt;     // b's K dim is the contiguous one (a transposed view)
+    bool bcast_b;  // the dps2/dps3 slice broadcast applies to the kernel's b
+                   // operand (operand-swapped problem), not to a
 };
 
 // Launch configuration chosen by the planner.

@@ -51,13 +51,18 @@ def contiguous_nb(elem_bytes: int, row_nbytes: int, ne1: int, ne2: int) -> list:
     return [elem_bytes, row_nbytes, row_nbytes * ne1, row_nbytes * ne1 * ne2]
 
 
-def make_ne_nb(a_type: int, a_ne, b_ne):
-    """ne[12], nb[12] for contiguous a, b and dst of the given shapes."""
+def make_ne_nb(a_type: int, a_ne, b_ne, b_kt: bool = False):
+    """ne[12], nb[12] for contiguous a, b and dst of the given shapes.  With
+    b_kt, b is stored K-contiguous: numpy shape (ne13, ne12, ne10, K), the
+    transposed view a matmul backward passes for the input gradient."""
     ne00, K, ne02, ne03 = (int(x) for x in a_ne)
     ne10, K1, ne12, ne13 = (int(x) for x in b_ne)
     ne = [ne00, K, ne02, ne03, ne10, K1, ne12, ne13, ne00, ne10, ne12, ne13]
     nb_a = contiguous_nb(BLOCK_BYTES[a_type], row_bytes(a_type, ne00), K, ne02)
-    nb_b = contiguous_nb(4, 4 * ne10, K1, ne12)
+    if b_kt:
+        nb_b = [4 * K1, 4, 4 * K1 * ne10, 4 * K1 * ne10 * ne12]
+    else:
+        nb_b = contiguous_nb(4, 4 * ne10, K1, ne12)
     nb_d = contiguous_nb(4, 4 * ne00, ne10, ne12)
     return ne, nb_a + nb_b + nb_d
 
@@ -141,14 +146,19 @@ class Instance:
     meta: dict = field(default_factory=dict)
 
     @property
+    def b_kt(self):
+        return self.nb[5] == 4 and self.nb[4] != 4
+
+    @property
     def dst_shape(self):
         ne = self.ne
         return (ne[11], ne[10], ne[9], ne[8])
 
 
 def make_instance(name: str, a_type: int, a_ne, b_ne, seed: int, a_std: float = 1.0,
-                  b_kind: str = "normal", note: str = "") -> Instance:
-    """Draw a, then b (then b's outliers), from PCG64(seed)."""
+                  b_kind: str = "normal", note: str = "", b_kt: bool = False) -> Instance:
+    """Draw a, then b (then b's outliers), from PCG64(seed).  b_kt stores the
+    same b values K-contiguous (numpy shape (ne13, ne12, ne10, K))."""
     ne00, K, ne02, ne03 = (int(x) for x in a_ne)
     ne10, _, ne12, ne13 = (int(x) for x in b_ne)
     rng = rng_for(seed)
@@ -162,7 +172,9 @@ def make_instance(name: str, a_type: int, a_ne, b_ne, seed: int, a_std: float = 
         b = gradient_like_f32(rng, (ne13, ne12, K, ne10))
     else:
         raise ValueError(b_kind)
-    ne, nb = make_ne_nb(a_type, a_ne, b_ne)
+    if b_kt:
+        b = np.ascontiguousarray(b.transpose(0, 1, 3, 2))
+    ne, nb = make_ne_nb(a_type, a_ne, b_ne, b_kt)
     return Instance(name, a_type, a, b, ne, nb, seed, note)
 
 

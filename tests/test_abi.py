@@ -59,7 +59,7 @@ def test_valid_problem_plans():
     (lambda ne, nb: ne.__setitem__(9, 2561), "E_DST_SHAPE"),
     (lambda ne, nb: ne.__setitem__(0, -1), "E_SHAPE"),
     (lambda ne, nb: nb.__setitem__(0, 8), "E_LAYOUT"),      # a not unit stride
-    (lambda ne, nb: nb.__setitem__(4, 2048), "E_LAYOUT"),   # transposed b view
+    (lambda ne, nb: nb.__setitem__(4, 2048), "E_LAYOUT"),   # neither b dim contiguous
     (lambda ne, nb: nb.__setitem__(8, 8), "E_LAYOUT"),
     (lambda ne, nb: nb.__setitem__(5, 10242), "E_LAYOUT"),  # misaligned stride
     (lambda ne, nb: nb.__setitem__(9, 16), "E_LAYOUT"),     # dst rows overlap
@@ -162,3 +162,34 @@ def test_forced_kernels():
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, 40))] == "E_KERNEL"
+
+
+def test_k_contiguous_b_layout():
+    """b as a transposed view (K contiguous) is accepted by both families;
+    wide-strip column configurations refuse it."""
+    ne, nb = synth.make_ne_nb(synth.Q4_K, (512, 64, 1, 1), (16, 64, 1, 1), b_kt=True)
+    assert nb[4] == 4 * 64 and nb[5] == 4
+    p = B.out_prod_plan(A, synth.Q4_K, BB, D, ne, nb)
+    assert p["kernel_name"] == "tiled"
+    ne, nb = synth.make_ne_nb(synth.F32, (8, 512, 1, 1), (2560, 512, 1, 1), b_kt=True)
+    p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb)
+    assert p["kernel_name"] == "skinny" and p["tile_n"] == 16
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 2))] == "E_KERNEL"
+    assert plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 6)) == 0
+    # b's extent with the K-contiguous layout: dst right after b's last byte is fine,
+    # dst on b's last float aliases
+    last = BB + 4 * 512 * 2560
+    assert plan(synth.F32, ne, nb, d=last) == 0
+    assert B.STATUS[plan(synth.F32, ne, nb, d=last - 4)] == "E_ALIAS"
+
+
+def test_narrow_b_runs_operand_swapped():
+    """A narrow f32 b with a wide f32 a (a LoRA down-projection's gradient
+    out_prod(x, grad_h)) runs the column kernel on the swapped problem."""
+    ne, nb = synth.make_ne_nb(synth.F32, (2560, 512, 1, 1), (8, 512, 1, 1))
+    p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb)
+    assert p["kernel_name"] == "skinny" and p["swapped"] == 1
+    ne, nb = synth.make_ne_nb(synth.F32, (2560, 512, 1, 1), (8, 512, 1, 1), b_kt=True)
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["swapped"] == 0
+    ne, nb = synth.make_ne_nb(synth.Q8_0, (2560, 512, 1, 1), (8, 512, 1, 1))
+    assert B.out_prod_plan(A, synth.Q8_0, BB, D, ne, nb)["swapped"] == 0

@@ -328,3 +328,80 @@ def test_graph_capture_replays_match_eager():
             assert np.array_equal(got, ref * np.float32(scale)), (name, rep)
             b_d.mul_(2.0)          # eager work on the captured buffer
             scale *= 2.0
+
+
+# ---------------------------------------------------------------- b as a transposed view
+
+KT_CASES = [
+    (synth.F32, (8, 517, 1, 1), (333, 517, 1, 1)),
+    (synth.F32, (4, 64, 1, 1), (100, 64, 1, 1)),       # K % 16 == 0: vector path
+    (synth.F32, (24, 130, 2, 1), (70, 130, 4, 1)),
+    (synth.F32, (300, 45, 2, 1), (290, 45, 4, 1)),
+    (synth.Q8_0, (352, 70, 1, 1), (150, 70, 1, 1)),
+    (synth.Q4_K, (768, 37, 1, 2), (141, 37, 1, 2)),
+    (synth.Q4_K, (512, 64, 1, 1), (130, 64, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("a_type,a_ne,b_ne", KT_CASES)
+def test_k_contiguous_b(a_type, a_ne, b_ne):
+    """b stored K-contiguous (the grad^T view of the matmul backward)."""
+    inst = synth.make_instance("kt", a_type, a_ne, b_ne, seed_of("kt", a_ne, b_ne), b_kt=True)
+    assert inst.b_kt
+    check_case(inst)
+
+
+@pytest.mark.parametrize("cfg", range(10))
+def test_k_contiguous_b_every_tiled_configuration(cfg):
+    code = B.kernel_code(B.KERNEL_TILED, cfg)
+    for a_type, a_ne, b_ne in KT_CASES[3:]:
+        inst = synth.make_instance("ktcfg", a_type, a_ne, b_ne, seed_of("ktc", cfg, a_ne), b_kt=True)
+        check_case(inst, code)
+
+
+@pytest.mark.parametrize("cfg", [0, 5, 6])
+def test_k_contiguous_b_column_configurations(cfg):
+    code = B.kernel_code(B.KERNEL_SKINNY, cfg)
+    for a_type, a_ne, b_ne in KT_CASES[:4]:
+        inst = synth.make_instance("ktcol", a_type, a_ne, b_ne, seed_of("ktcol", cfg, a_ne), b_kt=True)
+        check_case(inst, code)
+    # misaligned b: scalar loads
+    inst = synth.make_instance("ktmis", synth.F32, (8, 64, 1, 1), (40, 64, 1, 1), cfg, b_kt=True)
+    gpu = G.run(inst.a, synth.F32, inst.b, inst.ne, inst.nb, code, b_off=4)
+    ref, den = oracle.out_prod(inst.a, synth.F32, inst.b, inst.ne, inst.nb)
+    assert oracle.check(gpu, ref, den, TOL)["ok"]
+
+
+@pytest.mark.parametrize("name", ["q4_K_5120x17408", "q4_K_17408x5120", "q8_0_5120", "lora_r8_9216"])
+def test_k_contiguous_b_full_size(name):
+    """Input gradient through a frozen weight, out_prod(W, grad^T), at full size."""
+    a_type, a_ne, b_ne, seed, a_std, b_kind = synth.WORKLOADS[name][:6]
+    inst = synth.make_instance(name + "_kt", a_type, a_ne, b_ne, seed, a_std, b_kind, b_kt=True)
+    n = b_ne[0]
+    cols = None
+    if inst.ne[0] * inst.ne[1] * n > 5e9:
+        cols = np.array([[i1, 0, 0] for i1 in (0, 1, n // 3, n - 1)])
+    check_case(inst, 0, cols)
+
+
+# ---------------------------------------------------------------- narrow b (operand swap)
+
+@pytest.mark.parametrize("a_ne,b_ne", [
+    ((2560, 512, 1, 1), (8, 512, 1, 1)),     # LoRA down-projection gradient out_prod(x, grad_h)
+    ((300, 77, 2, 1), (8, 77, 4, 1)),        # broadcast on the wide operand
+    ((130, 33, 1, 3), (24, 33, 2, 3)),
+    ((40, 5, 1, 1), (1, 5, 1, 1)),
+])
+def test_narrow_b_operand_swap(a_ne, b_ne):
+    inst = synth.make_instance("nb", synth.F32, a_ne, b_ne, seed_of("nb", a_ne))
+    p = B.out_prod_plan(0x10000000, synth.F32, 0x40000000000, 0x80000000000, inst.ne, inst.nb)
+    assert p["swapped"] == 1
+    check_case(inst)
+    # dst with padded rows (the swapped store walks dst's strides)
+    nb = list(inst.nb)
+    nb[9] = 4 * a_ne[0] + 20
+    nb[10] = nb[9] * b_ne[0] + 8
+    nb[11] = nb[10] * b_ne[2]
+    gpu = G.run(inst.a, synth.F32, inst.b, inst.ne, nb)
+    ref, den = oracle.out_prod(inst.a, synth.F32, inst.b, inst.ne, nb)
+    assert oracle.check(gpu, ref, den, TOL)["ok"]
