@@ -42,6 +42,10 @@ RIDGE = PEAK_MFMA_F32_TFLOPS * 1e3 / PEAK_HBM_GBPS   # flop per byte
 COMPOSITE = {
     "q4_K_27B_both": ["q4_K_5120x17408", "q4_K_17408x5120"],
 }
+# The five OUT_PRODs of one LoRA-adapted linear layer's backward (frozen q4_K
+# weight, rank 8): input gradient through W and through A, the gradient of
+# the rank-8 activation, and the two adapter gradients.
+COMPOSITE.update({name: list(group) for name, group in synth.LORA_BACKWARD.items()})
 DEFAULT_WORKLOAD = "q4_K_27B_both"
 
 # The pages' per-op float-staging times for the same q4_K x f32 shapes
@@ -173,6 +177,11 @@ def main():
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(stream)
+    # one uncaptured step on the capture stream first: a launch that splits K
+    # allocates that stream's workspace on its first call
+    for j in range(len(insts)):
+        launch(0, j, cap.cuda_stream)
+    torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=cap):
         cptr = torch.cuda.current_stream(dev).cuda_stream
         for s in range(K):
@@ -193,15 +202,44 @@ def main():
     log("timed %d steps (graph): %.4f ms/step; eager %.4f ms/step (host wall %.3f s)"
         % (K, ms_step, ms_eager, wall))
 
-    # dominant kernel: all launches of a workload run one kernel family; its
-    # average launch duration is the graph's time per launch
-    flops_launch = np.array([w[0] for w in work], dtype=np.float64)
-    bytes_launch = np.array([w[1] for w in work], dtype=np.float64)
-    ai = flops_step / bytes_step
+    # Per-launch durations: each launch of the step alone, K times in a graph
+    # of its own (rotating inputs as above), timed with HIP events.
+    launch_us = []
+    for j in range(len(insts)):
+        g = torch.cuda.CUDAGraph()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            cptr = torch.cuda.current_stream(dev).cuda_stream
+            for s in range(K):
+                launch(s % R, j, cptr)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        launch_us.append(t0.elapsed_time(t1) / K * 1e3)
+        del g
+    log("per-launch us:", ["%s %.2f" % (i.name, u) for i, u in zip(insts, launch_us)])
+
+    # Dominant kernel: the kernel family with the largest share of the step.
+    # When every launch runs that family, its average launch duration is the
+    # timed region's time per launch; otherwise it is the per-launch pass's.
+    kname = [p[3]["kernel_name"] for p in sets[0]]
+    share = {k: sum(u for u, n in zip(launch_us, kname) if n == k) for k in set(kname)}
+    dom = max(share, key=share.get)
+    sel = [j for j in range(len(insts)) if kname[j] == dom]
+    flops_launch = np.array([work[j][0] for j in sel], dtype=np.float64)
+    bytes_launch = np.array([work[j][1] for j in sel], dtype=np.float64)
+    ai = flops_launch.sum() / bytes_launch.sum()
     bound = "mfma" if ai >= RIDGE else "hbm"
-    kernels = sorted(set(p[3]["kernel_name"] for p in sets[0]))
+    kernels = [dom]
     # algorithmic work per launch / the kernel's average launch duration
-    mean_s = ms_step / len(insts) * 1e-3
+    if len(sel) == len(insts):
+        mean_s = ms_step / len(insts) * 1e-3
+    else:
+        mean_s = float(np.mean([launch_us[j] for j in sel])) * 1e-6
     if bound == "mfma":
         achieved = float(flops_launch.mean()) / mean_s / 1e12
         peak, unit = PEAK_MFMA_F32_TFLOPS, "TFLOP/s"
@@ -216,7 +254,8 @@ def main():
     roofline = {
         "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
         "frac": round(achieved / peak, 4), "traffic": traffic,
-        "kernel": kernels[0] if len(kernels) == 1 else kernels,
+        "kernel": dom,
+        "launches_of_kernel": [insts[j].name for j in sel],
         "avg_launch_us": round(mean_s * 1e6, 3),
         "algorithmic_flops_per_launch": [int(x) for x in flops_launch],
         "algorithmic_bytes_per_launch": [int(x) for x in bytes_launch],
@@ -242,7 +281,11 @@ def main():
             "workload": args.workload,
             "launches": [{"name": i.name, "a_type": synth.TYPE_NAMES[i.a_type],
                           "ne00": i.ne[0], "K": i.ne[1], "ne10": i.ne[4],
-                          "slices": i.ne[10] * i.ne[11]} for i in insts],
+                          "slices": i.ne[10] * i.ne[11],
+                          "b_layout": "k_contiguous" if i.b_kt else "row",
+                          "kernel": p[3]["kernel_name"], "variant": p[3]["variant"],
+                          "swapped": bool(p[3]["swapped"]), "us": round(u, 3)}
+                         for i, p, u in zip(insts, sets[0], launch_us)],
             "rotating_input_sets": R,
         },
         "gbps": round(gbps, 1),

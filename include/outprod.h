@@ -33,12 +33,32 @@
  *            (2 for q8_0 a).  dst's dims must be ordered and must not overlap.
  *
  * Memory and ownership: a, b and dst are DEVICE pointers owned by the caller.
- * The library keeps no pointer after a call returns, allocates nothing and
- * holds no mutable state, so calls may come from any thread.  A call only
+ * The library keeps no pointer to them after a call returns.  A call only
  * enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
  * returns; the buffers must stay alive until the stream has passed it.
  * dst is overwritten (not accumulated into).  Results are deterministic:
- * every dst element has one writer and a fixed summation order.
+ * every dst element has one writer and a fixed summation order, also when K
+ * is split (see below).
+ *
+ * Split K and the workspace: when a problem has too few output tiles to fill
+ * the GPU but a long K, the library splits K into ranges (outprod_plan.splits)
+ * that run in parallel and write partial results to a workspace; a second
+ * kernel on the same stream adds the partials in range order into dst.  The
+ * workspace (64 MiB) belongs to the library, one per (device, stream) pair,
+ * allocated with hipMalloc by the first call on that stream whose plan splits
+ * K and kept until the process ends (never freed, so a captured graph that
+ * uses it stays valid).  Consequences:
+ *   - Calls on one stream are ordered by the stream; calls on different
+ *     streams use different workspaces and may overlap.  A HIP graph keeps
+ *     using the workspace of the stream it was captured on: do not replay it
+ *     concurrently with calls on that stream or with another replay of a
+ *     graph captured there.
+ *   - The allocation cannot happen while the stream is being captured: a
+ *     splitting call on a capturing stream that has no workspace yet returns
+ *     OUTPROD_E_CAPTURE without enqueuing anything.  One uncaptured call on
+ *     that stream beforehand (any splitting problem) avoids it.
+ * The library's only mutable state is that table, guarded by a mutex; calls
+ * may come from any thread.
  *
  * Errors: every function returns OUTPROD_OK (0) or a negative status.  All
  * argument checks happen on the host before any HIP call, and on error dst
@@ -77,7 +97,10 @@ extern "C" {
 #define OUTPROD_E_ALIAS (-9)     /* dst's bytes overlap a's or b's */
 #define OUTPROD_E_RANGE (-10)    /* an extent overflows the kernels' index range */
 #define OUTPROD_E_KERNEL (-11)   /* a forced kernel that cannot run this problem */
-#define OUTPROD_E_HIP (-12)      /* the kernel launch failed (e.g. no gfx950 device) */
+#define OUTPROD_E_HIP (-12)      /* a HIP call failed: kernel launch (e.g. no gfx950
+                                    device) or the workspace allocation */
+#define OUTPROD_E_CAPTURE (-13)  /* the plan splits K, the stream is capturing a graph and
+                                    has no workspace yet (see "Split K" above) */
 
 /*
  * out_prod: dst = OUT_PROD(a, b) as defined above, enqueued on `stream`.
@@ -116,6 +139,10 @@ typedef struct outprod_plan {
     int variant;      /* configuration index within the family */
     int swapped;      /* 1: run as the operand-swapped problem (narrow f32 b with a
                          wide f32 a); tile_m then runs along ne10, tile_n along ne00 */
+    int splits;       /* K ranges run in parallel (1: no split, no reduce kernel) */
+    int64_t ksplit;   /* K rows per range (the last range may be shorter) */
+    int64_t workspace_bytes; /* partial results: splits * ne00 * ne10 * slices * 4
+                                (0 without a split); at most 64 MiB */
 } outprod_plan;
 
 /*
@@ -134,9 +161,13 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
  * _SKINNY or _TILED), for A/B measurements and for testing both kernels on
  * the same problem.  Bits 8-15 of `kernel` may force a configuration of the
  * family: (index + 1) << 8, with the index as reported in
- * outprod_plan.variant; 0 lets the library choose.  A family or
- * configuration that cannot run the problem returns OUTPROD_E_KERNEL (e.g.
- * SKINNY for a quantized a, or an unknown configuration index).
+ * outprod_plan.variant; 0 lets the library choose.  Bits 16-23 may force
+ * the split count of K (with a forced family only): 1 = no split, n = n
+ * ranges of ceil(K/n) rows (fewer when K is short); 0 lets the library
+ * choose.  A family, configuration or split that cannot run the problem
+ * returns OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a, an unknown
+ * configuration index, more ranges than K rows or partials beyond the
+ * workspace).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);
@@ -144,7 +175,7 @@ int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
 /* A static English description of a status code; never NULL. */
 const char *out_prod_strerror(int status);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2 (1 had no split fields in outprod_plan). */
 int out_prod_version(void);
 
 #ifdef __cplusplus

@@ -32,15 +32,18 @@ OUTPROD_OK = 0
 STATUS = {
     -1: "E_NULL", -2: "E_TYPE", -3: "E_SHAPE", -4: "E_K", -5: "E_DST_SHAPE", -6: "E_BCAST",
     -7: "E_QK", -8: "E_LAYOUT", -9: "E_ALIAS", -10: "E_RANGE", -11: "E_KERNEL", -12: "E_HIP",
+    -13: "E_CAPTURE",
 }
 KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
 
 
-def kernel_code(family: int, config: int = None) -> int:
+def kernel_code(family: int, config: int = None, splits: int = None) -> int:
     """out_prod_ex's kernel argument: a family, optionally with a forced
-    configuration index (as reported by out_prod_plan's ``variant``)."""
-    return family | ((config + 1) << 8 if config is not None else 0)
+    configuration index (as reported by out_prod_plan's ``variant``) and a
+    forced split count of K (1 = no split)."""
+    code = family | ((config + 1) << 8 if config is not None else 0)
+    return code | (splits << 16 if splits is not None else 0)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
 
@@ -59,7 +62,8 @@ class outprod_plan(ctypes.Structure):
                 ("tile_k", ctypes.c_int), ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
                 ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int),
-                ("swapped", ctypes.c_int)]
+                ("swapped", ctypes.c_int), ("splits", ctypes.c_int), ("ksplit", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 _I64x12 = ctypes.c_int64 * 12

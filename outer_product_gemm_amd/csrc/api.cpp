@@ -12,6 +12,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include <hip/hip_runtime_api.h>
 
 #include "outprod.h"
@@ -204,12 +207,17 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
         return l.grid > lim ? OUTPROD_E_RANGE : OUTPROD_OK;
     }
 
-    // kernel = family | (tile configuration + 1) << 8; configuration 0 = automatic
+    // kernel = family | (tile configuration + 1) << 8 | splits << 16;
+    // configuration 0 and splits 0 = automatic
     const int variant = (kernel >> 8) & 0xFF;
+    const int splits = (kernel >> 16) & 0xFF;
+    if (kernel >> 24) return OUTPROD_E_KERNEL;
     kernel &= 0xFF;
-    if (variant != 0 && kernel != OUTPROD_KERNEL_TILED && kernel != OUTPROD_KERNEL_SKINNY)
+    if ((variant != 0 || splits != 0) && kernel != OUTPROD_KERNEL_TILED &&
+        kernel != OUTPROD_KERNEL_SKINNY)
         return OUTPROD_E_KERNEL;
     l.variant = variant;
+    l.splits = splits;
     bool ok;
     switch (kernel) {
     case OUTPROD_KERNEL_AUTO: {
@@ -226,7 +234,8 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
             c->p = swap_operands(p);
             c->swapped = true;
             ok = plan_skinny(c->p, &l);
-        } else if (f32 && (!tiled_ok || t.grid < 128)) {
+        } else if (f32 && (!tiled_ok || t.grid / t.splits < 128)) {
+            // (output tiles counted without K splits)
             ok = plan_skinny(p, &l);
         } else {
             l = t;
@@ -248,12 +257,50 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     return OUTPROD_OK;
 }
 
+// The split-K workspaces: one per (device, stream), allocated on first use
+// and never freed (graphs captured on the stream keep their address).
+struct Workspace {
+    int device;
+    hipStream_t stream;
+    uint8_t *ptr;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+int stream_workspace(hipStream_t stream, uint8_t **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return OUTPROD_E_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    for (const Workspace &w : g_ws) {
+        if (w.device == dev && w.stream == stream) {
+            *out = w.ptr;
+            return OUTPROD_OK;
+        }
+    }
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return OUTPROD_E_HIP;
+    if (st != hipStreamCaptureStatusNone) return OUTPROD_E_CAPTURE;
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, (size_t)kWorkspaceBytes) != hipSuccess) return OUTPROD_E_HIP;
+    g_ws.push_back(Workspace{dev, stream, (uint8_t *)ptr});
+    *out = (uint8_t *)ptr;
+    return OUTPROD_OK;
+}
+
 int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne,
         const int64_t *nb, void *stream, int kernel) {
     Checked c;
     int rc = validate_and_plan(a, a_type, b, dst, ne, nb, kernel, &c);
     if (rc != OUTPROD_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
+    if (c.l.splits > 1) {
+        uint8_t *ws = nullptr;
+        rc = stream_workspace(s, &ws);
+        if (rc != OUTPROD_OK) return rc;
+        c.p.splits = c.l.splits;
+        c.p.ksplit = c.l.ksplit;
+        c.p.ws = ws;
+    }
     hipError_t e = hipSuccess;
     switch (c.l.kernel) {
     case OUTPROD_KERNEL_NONE:
@@ -270,6 +317,7 @@ int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne
     default:
         return OUTPROD_E_KERNEL;
     }
+    if (e == hipSuccess && c.p.splits > 1) e = launch_split_reduce(c.p, s);
     return e == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
 }
 
@@ -308,6 +356,9 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
     plan->flops = 2 * c.p.M * c.p.N * c.p.K * plan->slices;
     plan->variant = c.l.variant;
     plan->swapped = c.swapped ? 1 : 0;
+    plan->splits = c.l.splits > 1 ? c.l.splits : 1;
+    plan->ksplit = c.l.splits > 1 ? c.l.ksplit : c.p.K;
+    plan->workspace_bytes = outprod::split_bytes(c.p, plan->splits);
     return OUTPROD_OK;
 }
 
@@ -325,11 +376,14 @@ const char *out_prod_strerror(int status) {
     case OUTPROD_E_ALIAS: return "dst overlaps an input";
     case OUTPROD_E_RANGE: return "extent exceeds the supported index range";
     case OUTPROD_E_KERNEL: return "the requested kernel cannot run this problem";
-    case OUTPROD_E_HIP: return "HIP kernel launch failed";
+    case OUTPROD_E_HIP: return "a HIP call failed (kernel launch or workspace allocation)";
+    case OUTPROD_E_CAPTURE:
+        return "K is split and the capturing stream has no workspace yet: make one uncaptured "
+               "call on this stream first";
     default: return "unknown status";
     }
 }
 
-int out_prod_version(void) { return 1; }
+int out_prod_version(void) { return 2; }
 
 }  // extern "C"

@@ -63,6 +63,24 @@ __device__ __forceinline__ SliceBase slice_base(const Problem &p, int z) {
     return s;
 }
 
+// Split K: narrow problem q (a copy of the launch's problem) and slice s to
+// contraction range `sp` -- rows [sp*ksplit, min(K, (sp+1)*ksplit)) -- whose
+// partial result goes to the dense [slices][N][M] block sp of the workspace.
+__device__ __forceinline__ void apply_split(Problem &q, SliceBase &s, int z, int sp) {
+    const int64_t kb = (int64_t)sp * q.ksplit;
+    const int64_t klen = q.K - kb < q.ksplit ? q.K - kb : q.ksplit;
+    s.a += kb * q.nb01;
+    s.b += kb * q.nb11;
+    const int64_t plane = q.M * q.N;
+    s.dst = q.ws + ((int64_t)sp * q.ne12 * q.ne13 + z) * plane * 4;
+    q.K = klen;
+    // K-contiguous b moves by kb floats: vector loads along k stay aligned
+    // only for kb a multiple of 4 (row-major b and a move by whole rows)
+    if (q.b_kt && (kb & 3) != 0) q.vec_b = false;
+    q.nb0 = 4;
+    q.nb1 = 4 * q.M;
+}
+
 __device__ __forceinline__ float ldf(const uint8_t *p) { return *(const float *)p; }
 
 }  // namespace outprod

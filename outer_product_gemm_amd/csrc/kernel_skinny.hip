@@ -196,15 +196,19 @@ __device__ __forceinline__ void column_k_loop_kt(const Problem &p, const SliceBa
 // MT: 16-column blocks of a; CW: columns of b per lane; W: waves; U: 4-row
 // steps per wave whose loads are issued together.
 template <int MT, int CW, int W, int U>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p, int col_blocks, int m_blocks) {
+__global__ __launch_bounds__(64 * W) void skinny_kernel(Problem p0, int col_blocks, int m_blocks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int n0 = (logical % col_blocks) * (16 * CW);
     const int rest = logical / col_blocks;
     const int m0 = (rest % m_blocks) * 16 * MT;
-    const int z = rest / m_blocks;
-    const SliceBase s = slice_base(p, z);
+    const int slices = (int)(p0.ne12 * p0.ne13);
+    const int zz = rest / m_blocks;
+    const int z = zz % slices, sp = zz / slices;  // split range outermost
+    Problem p = p0;
+    SliceBase s = slice_base(p, z);
+    if (p.splits > 1) apply_split(p, s, z, sp);
     const int M = (int)p.M, N = (int)p.N;
 
     floatx4 acc[CW][MT];
@@ -375,15 +379,19 @@ __device__ __forceinline__ void narrow_k_loop_kt(const Problem &p, const SliceBa
 
 // T4: 4-column blocks of a (4*T4 columns per workgroup); CW, W, U as above.
 template <int T4, int CW, int W, int U>
-__global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p, int col_blocks, int m_blocks) {
+__global__ __launch_bounds__(64 * W) void narrow_kernel(Problem p0, int col_blocks, int m_blocks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int n0 = (logical % col_blocks) * (16 * CW);
     const int rest = logical / col_blocks;
     const int m0 = (rest % m_blocks) * 4 * T4;
-    const int z = rest / m_blocks;
-    const SliceBase s = slice_base(p, z);
+    const int slices = (int)(p0.ne12 * p0.ne13);
+    const int zz = rest / m_blocks;
+    const int z = zz % slices, sp = zz / slices;  // split range outermost
+    Problem p = p0;
+    SliceBase s = slice_base(p, z);
+    if (p.splits > 1) apply_split(p, s, z, sp);
     const int M = (int)p.M, N = (int)p.N;
 
     floatx4 acc[CW][T4];
@@ -492,8 +500,25 @@ const void *narrow_dispatch(int t4, int c) {
 
 }  // namespace
 
-// l->variant on entry: forced configuration + 1, or 0 for automatic.  On
-// return: the configuration index (the i0 block width is tile_m).
+// Split count for a column launch of `grid` workgroups: when the strips
+// alone leave three quarters of the CUs idle (64 workgroups or fewer), split
+// K into ranges of at least 256 rows until the launch has about 256
+// workgroups (the partial tiles are small: M x N floats per range).  Measured
+// on MI355X: rank-8 gradients with K = 9216 / 17408 over 512 / 1024 columns
+// (32 / 64 strips) run 3x faster split; at 80 strips and K = 1024 the extra
+// reduce launch costs more than the split gains.
+int column_splits(const Problem &p, int64_t grid) {
+    if (grid > 64) return 1;
+    int64_t s = (256 + grid - 1) / grid;
+    if (s > p.K / 256) s = p.K / 256;
+    if (s > 64) s = 64;
+    while (s > 1 && split_bytes(p, (int)s) > kWorkspaceBytes) --s;
+    return s < 1 ? 1 : (int)s;
+}
+
+// l->variant on entry: forced configuration + 1, or 0 for automatic;
+// l->splits on entry: forced split count, or 0 for automatic.  On return:
+// the configuration index (the i0 block width is tile_m) and the split.
 bool plan_skinny(const Problem &p, Launch *l) {
     if (p.a_type != OUTPROD_TYPE_F32 || p.M < 1) return false;
     int cfg;
@@ -533,7 +558,20 @@ bool plan_skinny(const Problem &p, Launch *l) {
     l->tile_k = 4;
     l->block = 64 * c.waves;
     l->lds_bytes = c.waves * c.cw * (c.mma == 4 ? tile_m / 4 : tile_m / 16) * 256 * 4;
-    l->grid = col_blocks * m_blocks * p.ne12 * p.ne13;
+    const int64_t grid = col_blocks * m_blocks * p.ne12 * p.ne13;
+    int splits = l->splits;
+    int64_t ksplit = p.K;
+    if (splits > 0) {  // forced: even ranges of any row count
+        if (splits > p.K || (splits > 1 && split_bytes(p, splits) > kWorkspaceBytes)) return false;
+        if (splits > 1) ksplit = (p.K + splits - 1) / splits;
+    } else {
+        splits = column_splits(p, grid);
+        if (splits > 1) ksplit = split_rows(p.K, splits);
+    }
+    if (splits > 1) splits = (int)((p.K + ksplit - 1) / ksplit);
+    l->splits = splits > 1 ? splits : 1;
+    l->ksplit = splits > 1 ? ksplit : p.K;
+    l->grid = grid * l->splits;
     return true;
 }
 

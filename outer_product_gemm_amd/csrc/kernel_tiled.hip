@@ -342,7 +342,7 @@ __host__ __device__ constexpr int lds_ld(int bw, int mf) {
 // ---------------------------------------------------------------- kernel
 
 template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
-__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int tiles_m,
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int tiles_m,
                                                                int tiles_n) {
     typedef Mfma<MF> MM;
     constexpr int T = 64 * WGM * WGN;
@@ -358,9 +358,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p, int ti
     const int wm = wave % WGM, wn = wave / WGM;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int per_slice = tiles_m * tiles_n;
-    const int z = logical / per_slice, rem = logical % per_slice;
+    // split range outermost, so the tiles of one K range share the XCDs'
+    // caches as in an unsplit launch
+    const int slices = (int)(p0.ne12 * p0.ne13);
+    const int zz = logical / per_slice, rem = logical % per_slice;
+    const int z = zz % slices, sp = zz / slices;
     const int m0 = (rem % tiles_m) * BM, n0 = (rem / tiles_m) * BN;
-    const SliceBase s = slice_base(p, z);
+    Problem p = p0;
+    SliceBase s = slice_base(p, z);
+    if (p.splits > 1) apply_split(p, s, z, sp);
     const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
 
     typename ALoaderFor<AT, BM, BK, T>::type la;
@@ -513,33 +519,76 @@ const void *tiled_fn(int variant, bool bt) {
 
 // Estimated time of a configuration: the busiest CU runs ceil(tiles / 256)
 // tiles' worth of MFMA work at the configuration's efficiency.
-double cfg_cost(const TileCfg &c, const Problem &p) {
+// Rate unit of TileCfg::eff: tile area x K rows per microsecond on one CU
+// (the 27B q4_K shapes: 160 x 128 x 17408 per CU in 1647 us at eff 12.2).
+constexpr double kEffPerUs = 17.7e3;
+// Split-K overheads: the reduce kernel's launch gap and its traffic (every
+// partial read once, dst written once; the main kernel's extra partial writes
+// are counted with them) at a sustained rate in bytes per microsecond.
+constexpr double kSplitLaunchUs = 3.0;
+constexpr double kSplitBytesPerUs = 4.0e6;
+
+// Estimated time (us) of a configuration with `splits` K ranges: the
+// busiest CU runs ceil(tiles * splits / 256) tiles of ksplit rows each at
+// the configuration's efficiency, plus the split's reduction.
+double cfg_cost(const TileCfg &c, const Problem &p, int splits, int64_t ksplit) {
     const int64_t tiles = ((p.M + c.bm() - 1) / c.bm()) * ((p.N + c.bn() - 1) / c.bn()) * p.ne12 * p.ne13;
-    const int64_t per_cu = (tiles + 255) / 256;
-    return (double)per_cu * c.bm() * c.bn() / c.eff;
+    const int64_t per_cu = (tiles * splits + 255) / 256;
+    double t = (double)per_cu * c.bm() * c.bn() * (double)ksplit / c.eff / kEffPerUs;
+    if (splits > 1)
+        t += kSplitLaunchUs + (double)(2 * splits) * p.M * p.N * p.ne12 * p.ne13 * 4 / kSplitBytesPerUs;
+    return t;
+}
+
+// Split counts the planner considers: each range at least 256 rows.
+int max_splits(const Problem &p) {
+    int64_t s = p.K / 256;
+    if (s > 32) s = 32;
+    while (s > 1 && split_bytes(p, (int)s) > kWorkspaceBytes) --s;
+    return s < 1 ? 1 : (int)s;
 }
 
 }  // namespace
 
+// l->variant on entry: forced configuration + 1, or 0 for automatic;
+// l->splits on entry: forced split count, or 0 for automatic.
 bool plan_tiled(const Problem &p, Launch *l) {
-    int v = l->variant;  // forced configuration + 1, or 0 for automatic
-    int best;
-    if (v > 0) {
-        if (v > kNumCfgs) return false;
-        best = v - 1;
-    } else {
-        best = 0;
-        double best_cost = cfg_cost(kCfgs[0], p);
-        for (int i = 1; i < kNumCfgs; ++i) {
-            const double c = cfg_cost(kCfgs[i], p);
-            if (c < best_cost) {
+    int v = l->variant;
+    int best, best_splits = 1;
+    const int forced_splits = l->splits;
+    if (forced_splits > 0) {
+        if (forced_splits > 1 && split_bytes(p, forced_splits) > kWorkspaceBytes) return false;
+        if (forced_splits > p.K) return false;
+    }
+    // candidate split counts: forced, or 1 .. max_splits
+    const int s_lo = forced_splits > 0 ? forced_splits : 1;
+    const int s_hi = forced_splits > 0 ? forced_splits : max_splits(p);
+    const int c_lo = v > 0 ? v - 1 : 0, c_hi = v > 0 ? v - 1 : kNumCfgs - 1;
+    if (v > kNumCfgs) return false;
+    best = c_lo;
+    double best_cost = 0;
+    bool first = true;
+    for (int i = c_lo; i <= c_hi; ++i) {
+        for (int sp = s_lo; sp <= s_hi; ++sp) {
+            const int64_t ks = forced_splits > 0 ? (p.K + sp - 1) / sp : split_rows(p.K, sp);
+            const double c = cfg_cost(kCfgs[i], p, sp, ks);
+            if (first || c < best_cost) {
                 best = i;
+                best_splits = sp;
                 best_cost = c;
+                first = false;
             }
         }
     }
     const TileCfg &c = kCfgs[best];
     const int64_t tm = (p.M + c.bm() - 1) / c.bm(), tn = (p.N + c.bn() - 1) / c.bn();
+    int64_t ksplit = p.K;
+    if (best_splits > 1) {
+        // forced counts split K evenly (any row count); automatic ones in
+        // 64-row multiples, after which the count is what K needs
+        ksplit = forced_splits > 0 ? (p.K + best_splits - 1) / best_splits : split_rows(p.K, best_splits);
+        best_splits = (int)((p.K + ksplit - 1) / ksplit);
+    }
     l->kernel = OUTPROD_KERNEL_TILED;
     l->variant = best;
     l->tile_m = c.bm();
@@ -547,7 +596,9 @@ bool plan_tiled(const Problem &p, Launch *l) {
     l->tile_k = c.bk;
     l->block = c.threads();
     l->lds_bytes = 2 * c.bk * (lds_ld(c.bm(), c.mf) + lds_ld(c.bn(), c.mf)) * 4;
-    l->grid = tm * tn * p.ne12 * p.ne13;
+    l->splits = best_splits;
+    l->ksplit = best_splits > 1 ? ksplit : p.K;
+    l->grid = tm * tn * p.ne12 * p.ne13 * best_splits;
     return true;
 }
 

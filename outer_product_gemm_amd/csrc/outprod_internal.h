@@ -27,7 +27,22 @@ struct Problem {
     bool b_kt;     // b's K dim is the contiguous one (a transposed view)
     bool bcast_b;  // the dps2/dps3 slice broadcast applies to the kernel's b
                    // operand (operand-swapped problem), not to a
+    // Split K: splits > 1 runs the contraction as `splits` ranges of ksplit
+    // rows (the last one shorter); range s writes its partial dst, dense
+    // [slices][N][M] fp32, at ws + s * M*N*slices*4, and the reduce kernel
+    // adds the partials in range order into dst.
+    int splits;
+    int64_t ksplit;
+    uint8_t *ws;
 };
+
+// Bytes of the per-(device, stream) workspace; split plans never need more.
+constexpr int64_t kWorkspaceBytes = 64ll << 20;
+
+// Workspace bytes a split plan needs (0 without a split).
+inline int64_t split_bytes(const Problem &p, int splits) {
+    return splits > 1 ? (int64_t)splits * p.M * p.N * p.ne12 * p.ne13 * 4 : 0;
+}
 
 // Launch configuration chosen by the planner.
 struct Launch {
@@ -36,7 +51,9 @@ struct Launch {
     int tile_m, tile_n, tile_k;
     int block;
     int lds_bytes;
-    int64_t grid;
+    int64_t grid;     // main kernel workgroups (all splits)
+    int splits;       // 1 = no split
+    int64_t ksplit;   // rows per split
 };
 
 // Per-kernel planning (host only, no HIP calls) and launching.
@@ -47,5 +64,13 @@ void plan_zero(const Problem &p, Launch *l);
 hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s);
 hipError_t launch_tiled(const Problem &p, const Launch &l, hipStream_t s);
 hipError_t launch_zero(const Problem &p, const Launch &l, hipStream_t s);
+hipError_t launch_split_reduce(const Problem &p, hipStream_t s);
+
+// K rows per split for `splits` ranges: a multiple of 64 (keeps 16-byte
+// alignment of K-contiguous b and whole MFMA stages).
+inline int64_t split_rows(int64_t K, int splits) {
+    const int64_t r = (K + splits - 1) / splits;
+    return (r + 63) / 64 * 64;
+}
 
 }  // namespace outprod

@@ -199,6 +199,43 @@ WORKLOADS = {
 }
 
 
+# The backward of one LoRA-adapted linear layer y = W x + B (A x) with W a
+# frozen q4_K weight (in -> out), A [in -> r], B [r -> out], over T tokens.
+# The matmul backward is entirely OUT_PROD (pages: "metal: OUT_PROD multiplies in
+# float staging", body): the input gradient through a weight is
+# out_prod(weight, grad^T) -- b is the transposed (K-contiguous) view of the
+# gradient -- and a weight's gradient is out_prod(input, grad).
+#   dx_W = out_prod(W, gy^T)   a: q4_K [in, out]   b: [T, out] K-contiguous
+#   dB   = out_prod(h, gy)     a: [r, T]           b: [out, T]
+#   dh   = out_prod(B, gy^T)   a: [r, out]         b: [T, out] K-contiguous
+#   dA   = out_prod(x, dh)     a: [in, T]          b: [r, T]   (narrow b)
+#   dx_A = out_prod(A, dh^T)   a: [in, r]          b: [T, r]   K-contiguous
+def lora_linear_backward(prefix: str, n_in: int, n_out: int, rank: int, tokens: int, seed: int):
+    return {
+        prefix + "_dxW": (Q4_K, (n_in, n_out, 1, 1), (tokens, n_out, 1, 1), seed, 1.0, "normal",
+                          "input gradient through the frozen q4_K weight", True),
+        prefix + "_dB": (F32, (rank, tokens, 1, 1), (n_out, tokens, 1, 1), seed + 1, 0.02, "normal",
+                         "LoRA B gradient", False),
+        prefix + "_dh": (F32, (rank, n_out, 1, 1), (tokens, n_out, 1, 1), seed + 2, 0.02, "normal",
+                         "gradient of the rank-r activation", True),
+        prefix + "_dA": (F32, (n_in, tokens, 1, 1), (rank, tokens, 1, 1), seed + 3, 1.0, "normal",
+                         "LoRA A gradient (narrow b)", False),
+        prefix + "_dxA": (F32, (n_in, rank, 1, 1), (tokens, rank, 1, 1), seed + 4, 0.02, "normal",
+                          "input gradient through A", True),
+    }
+
+
+LORA_BACKWARD = {
+    "lora_4B_linear_backward": lora_linear_backward("lora4B", 2560, 9216, 8, 512, 61),
+    "lora_27B_linear_backward": lora_linear_backward("lora27B", 5120, 17408, 8, 1024, 71),
+}
+for _group in LORA_BACKWARD.values():
+    WORKLOADS.update(_group)
+
+
 def workload(name: str, seed: int = None) -> Instance:
-    a_type, a_ne, b_ne, s, a_std, b_kind, note = WORKLOADS[name]
-    return make_instance(name, a_type, a_ne, b_ne, s if seed is None else seed, a_std, b_kind, note)
+    spec = WORKLOADS[name]
+    a_type, a_ne, b_ne, s, a_std, b_kind, note = spec[:7]
+    b_kt = spec[7] if len(spec) > 7 else False
+    return make_instance(name, a_type, a_ne, b_ne, s if seed is None else seed, a_std, b_kind, note,
+                         b_kt=b_kt)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.out_prod_version() == 1
+    assert B.out_prod_version() == 2
     for code in [0] + list(B.STATUS):
         msg = B.out_prod_strerror(code)
         assert msg and msg != "unknown status"
@@ -193,3 +193,43 @@ def test_narrow_b_runs_operand_swapped():
     assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["swapped"] == 0
     ne, nb = synth.make_ne_nb(synth.Q8_0, (2560, 512, 1, 1), (8, 512, 1, 1))
     assert B.out_prod_plan(A, synth.Q8_0, BB, D, ne, nb)["swapped"] == 0
+
+
+def test_split_k_plans():
+    """Long-K problems with few output tiles split K; the plan reports the
+    ranges and the workspace; forced split counts are honoured or refused."""
+    # 4B-scale input gradient through a frozen q4_K weight: 64 tiles of 160 x 128
+    ne, nb = synth.make_ne_nb(synth.Q4_K, (2560, 9216, 1, 1), (512, 9216, 1, 1), b_kt=True)
+    p = B.out_prod_plan(A, synth.Q4_K, 0x40000000000, 0x80000000000, ne, nb)
+    assert p["kernel_name"] == "tiled" and p["splits"] > 1
+    assert p["ksplit"] % 64 == 0 and (p["splits"] - 1) * p["ksplit"] < 9216 <= p["splits"] * p["ksplit"]
+    assert p["workspace_bytes"] == p["splits"] * 2560 * 512 * 4 <= 64 << 20
+    tiles = -(-2560 // p["tile_m"]) * -(-512 // p["tile_n"])
+    assert p["grid"] == tiles * p["splits"]
+    # rank-8 gradient with a long K and few column strips
+    ne, nb = synth.make_ne_nb(synth.F32, (8, 9216, 1, 1), (512, 9216, 1, 1), b_kt=True)
+    p = B.out_prod_plan(A, synth.F32, 0x40000000000, 0x80000000000, ne, nb)
+    assert p["kernel_name"] == "skinny" and p["splits"] > 1 and p["ksplit"] >= 256
+    # the 27B q4_K products fill the chip unsplit
+    for name in ("q4_K_5120x17408", "q4_K_17408x5120", "q8_0_5120", "lora_r8_9216"):
+        a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
+        ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
+        p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
+        assert p["splits"] == 1 and p["workspace_bytes"] == 0 and p["ksplit"] == a_ne[1], name
+    # forced split counts (any row count), refused when impossible
+    ne, nb = base(a_ne=(40, 100, 1, 1), b_ne=(70, 100, 1, 1))
+    for fam in (B.KERNEL_TILED, B.KERNEL_SKINNY):
+        p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(fam, None, 3))
+        assert p["splits"] == 3 and p["ksplit"] == 34 and p["workspace_bytes"] == 3 * 40 * 70 * 4
+        p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(fam, None, 1))
+        assert p["splits"] == 1 and p["workspace_bytes"] == 0
+        assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(fam, None, 101))] == "E_KERNEL"
+    # 100 rows in 40 ranges: ceil(100/40) = 3 rows each, so 34 ranges
+    p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, None, 40))
+    assert p["ksplit"] == 3 and p["splits"] == 34
+    # partials beyond the 64 MiB workspace
+    ne, nb = base(a_ne=(4096, 100, 1, 1), b_ne=(4096, 100, 1, 1))
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, None, 2))] == "E_KERNEL"
+    # split bits need a forced family; bits above 23 are refused
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_AUTO, None, 2))] == "E_KERNEL"
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=1 << 24)] == "E_KERNEL"

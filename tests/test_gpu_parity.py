@@ -209,18 +209,21 @@ def test_deterministic_repeat():
 
 def test_broadcast_invariant_gpu():
     """Slices sharing i2/dps2 with identical b slices are bit-identical, and
-    each equals a one-slice call on (a[:,:,i2/dps2], b[:,:,i2])."""
+    each equals a one-slice call on (a[:,:,i2/dps2], b[:,:,i2]).  The split of
+    K depends on the launch size (a lone slice leaves CUs idle and is split),
+    so both calls pin the column kernel without a split."""
     inst = synth.workload("deltanet_bcast")
     b = inst.b.copy()
     b[0, 1] = b[0, 0]
     b[0, 6] = b[0, 0]   # another a slice (6 // 4 = 1)
-    gpu = G.run(inst.a, inst.a_type, b, inst.ne, inst.nb)
+    code = B.kernel_code(B.KERNEL_SKINNY, None, 1)
+    gpu = G.run(inst.a, inst.a_type, b, inst.ne, inst.nb, code)
     assert np.array_equal(gpu[0, 0], gpu[0, 1])
     assert not np.array_equal(gpu[0, 0], gpu[0, 6])
     ne1, nb1 = synth.make_ne_nb(synth.F32, (128, 512, 1, 1), (128, 512, 1, 1))
     for i2 in (0, 5, 15):
         one = G.run(np.ascontiguousarray(inst.a[:, i2 // 4]), synth.F32,
-                    np.ascontiguousarray(b[:, i2]), ne1, nb1)
+                    np.ascontiguousarray(b[:, i2]), ne1, nb1, code)
         assert np.array_equal(one[0, 0], gpu[0, i2])
 
 
@@ -405,3 +408,134 @@ def test_narrow_b_operand_swap(a_ne, b_ne):
     gpu = G.run(inst.a, synth.F32, inst.b, inst.ne, nb)
     ref, den = oracle.out_prod(inst.a, synth.F32, inst.b, inst.ne, nb)
     assert oracle.check(gpu, ref, den, TOL)["ok"]
+
+
+# ---------------------------------------------------------------- split K
+
+SPLIT_CASES = [
+    # (a_type, a_ne, b_ne, K-contiguous b, family, configuration or None, splits)
+    (synth.F32, (40, 300, 1, 1), (70, 300, 1, 1), False, B.KERNEL_TILED, None, 3),
+    # 61-row ranges: K-contiguous b loses 16-byte alignment past range 0
+    (synth.F32, (40, 301, 2, 1), (70, 301, 4, 1), True, B.KERNEL_TILED, None, 5),
+    (synth.F32, (130, 97, 1, 1), (129, 97, 1, 1), False, B.KERNEL_TILED, 1, 2),
+    (synth.F32, (8, 517, 1, 1), (333, 517, 1, 1), False, B.KERNEL_SKINNY, None, 4),
+    (synth.F32, (8, 517, 1, 1), (333, 517, 1, 1), True, B.KERNEL_SKINNY, None, 7),
+    (synth.F32, (24, 130, 2, 1), (70, 130, 4, 1), True, B.KERNEL_SKINNY, None, 2),
+    (synth.F32, (3, 200, 1, 2), (50, 200, 1, 2), False, B.KERNEL_SKINNY, 6, 6),
+    (synth.F32, (8, 300, 1, 1), (200, 300, 1, 1), False, B.KERNEL_SKINNY, 10, 3),
+    (synth.F32, (33, 150, 1, 1), (90, 150, 1, 1), False, B.KERNEL_SKINNY, 3, 5),
+    (synth.Q8_0, (352, 70, 1, 1), (150, 70, 1, 1), False, B.KERNEL_TILED, None, 2),
+    (synth.Q4_K, (768, 37, 1, 2), (141, 37, 1, 2), True, B.KERNEL_TILED, None, 3),
+    (synth.Q4_K, (512, 200, 1, 1), (130, 200, 1, 1), False, B.KERNEL_TILED, None, 64),
+]
+
+
+@pytest.mark.parametrize("a_type,a_ne,b_ne,kt,fam,cfg,splits", SPLIT_CASES)
+def test_split_k_forced(a_type, a_ne, b_ne, kt, fam, cfg, splits):
+    """K split into ranges whose partials the reduce kernel adds: parity with
+    the oracle, and two runs are bit-identical."""
+    inst = synth.make_instance("split", a_type, a_ne, b_ne, seed_of("split", a_ne, b_ne, kt), b_kt=kt)
+    code = B.kernel_code(fam, cfg, splits)
+    p = B.out_prod_plan(0x10000000, a_type, 0x40000000000, 0x80000000000, inst.ne, inst.nb, code)
+    assert p["splits"] > 1
+    gpu = check_case(inst, code)
+    again = G.run(inst.a, a_type, inst.b, inst.ne, inst.nb, code)
+    assert np.array_equal(gpu, again)
+
+
+def test_split_k_integer_exact_equals_unsplit():
+    """Integer data: every summation order is exact, so the split result equals
+    the unsplit one and the exact sum bit for bit."""
+    rng = np.random.default_rng(seed_of("split-int"))
+    for kt, fam in ((False, B.KERNEL_TILED), (True, B.KERNEL_TILED), (False, B.KERNEL_SKINNY),
+                    (True, B.KERNEL_SKINNY)):
+        M = 40 if fam == B.KERNEL_TILED else 8
+        inst = synth.make_instance("si", synth.F32, (M, 777, 1, 1), (90, 777, 1, 1), 5, b_kt=kt)
+        a = _int_f32(rng, inst.a.shape)
+        b = _int_f32(rng, (777, 90))
+        b_host = np.ascontiguousarray(b.T) if kt else b
+        exact = (b.astype(np.float64).T @ a[0, 0].astype(np.float64)).astype(np.float32)
+        one = G.run(a, synth.F32, b_host, inst.ne, inst.nb, B.kernel_code(fam, None, 1))
+        many = G.run(a, synth.F32, b_host, inst.ne, inst.nb, B.kernel_code(fam, None, 9))
+        assert np.array_equal(one[0, 0], exact) and np.array_equal(many[0, 0], exact)
+
+
+def test_split_k_operand_swapped_auto():
+    """A narrow f32 b with a long K: the operand-swapped column launch splits K,
+    and the reduce writes dst through the exchanged strides (padded rows too)."""
+    inst = synth.make_instance("nbs", synth.F32, (300, 2048, 1, 1), (8, 2048, 1, 1), seed_of("nbs"))
+    p = B.out_prod_plan(0x10000000, synth.F32, 0x40000000000, 0x80000000000, inst.ne, inst.nb)
+    assert p["swapped"] == 1 and p["splits"] > 1
+    check_case(inst)
+    nb = list(inst.nb)
+    nb[9] = 4 * 300 + 20
+    nb[10] = nb[9] * 8
+    nb[11] = nb[10]
+    gpu = G.run(inst.a, synth.F32, inst.b, inst.ne, nb)
+    ref, den = oracle.out_prod(inst.a, synth.F32, inst.b, inst.ne, nb)
+    assert oracle.check(gpu, ref, den, TOL)["ok"]
+
+
+def _hip():
+    import ctypes
+    lib = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
+    lib.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def test_split_k_in_graph_capture():
+    """A splitting call captured in a graph: on a stream that has never run a
+    splitting call, capture is refused with E_CAPTURE (nothing enqueued); after
+    one uncaptured call on that stream, every replay equals the eager result
+    (with eager work on the captured buffers between replays)."""
+    import ctypes
+    hip = _hip()
+    raw = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(raw)) == 0
+    try:
+        ext = torch.cuda.ExternalStream(raw.value)
+        for name in ("lora4B_dh", "lora4B_dxW"):
+            inst = synth.workload(name)
+            plan = B.out_prod_plan(0x10000000, inst.a_type, 0x40000000000, 0x80000000000, inst.ne, inst.nb)
+            assert plan["splits"] > 1
+            a_d = G.to_dev(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1))
+            b_d = G.to_dev(inst.b)
+            eager = torch.empty(inst.dst_shape, dtype=torch.float32, device="cuda:0")
+            out = torch.zeros_like(eager)
+            B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), eager.data_ptr(), inst.ne, inst.nb,
+                       torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            ref = eager.cpu().numpy()
+            args = (a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb)
+            if name == "lora4B_dh":
+                g0 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g0, stream=ext):
+                    out.zero_()
+                    st = B.out_prod_status(*args, raw.value)
+                assert B.STATUS[st] == "E_CAPTURE"
+                del g0
+                torch.cuda.synchronize()
+                ext.wait_stream(torch.cuda.current_stream())
+                B.out_prod(*args, raw.value)   # uncaptured: allocates the stream's workspace
+                torch.cuda.synchronize()
+                assert np.array_equal(out.cpu().numpy(), ref)
+            g = torch.cuda.CUDAGraph()
+            ext.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(g, stream=ext):
+                B.out_prod(*args, raw.value)
+            torch.cuda.synchronize()
+            scale = 1.0
+            for rep in range(4):
+                out.fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(out.cpu().numpy(), ref * np.float32(scale)), (name, rep)
+                b_d.mul_(2.0)
+                scale *= 2.0
+            del g
+            torch.cuda.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(raw)
