@@ -5,7 +5,7 @@ CPU-baseline leg of ``bench.py`` may import this package.  The GPU library and
 its Python binding never import it; the two implementations share no code.
 
 The arithmetic lives in ``oracle.c`` (plain C, OpenMP over output columns,
-double accumulation in ascending k, its own fp16 / q8_0 / q4_K decoders).
+double accumulation in ascending k, its own decoders of every a type).
 This module compiles it with gcc on first use, loads it with ctypes and adds
 the element-wise gate that a GPU result must pass:
 
@@ -28,9 +28,13 @@ import threading
 
 import numpy as np
 
-F32, Q8_0, Q4_K = 0, 8, 12
-BLOCK_VALUES = {F32: 1, Q8_0: 32, Q4_K: 256}
-BLOCK_BYTES = {F32: 4, Q8_0: 34, Q4_K: 144}
+# GGUF type ids of the a (src0) types the oracle decodes
+F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0 = 0, 1, 2, 3, 6, 7, 8
+Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 10, 11, 12, 13, 14, 30
+BLOCK_VALUES = {F32: 1, F16: 1, BF16: 1, Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32,
+                Q2_K: 256, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {F32: 4, F16: 2, BF16: 2, Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34,
+               Q2_K: 84, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")

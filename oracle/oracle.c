@@ -29,13 +29,36 @@
  * converts to float, which is that single round-to-nearest-even.
  *
  * Block layouts (the pages name the types -- a Q4_K_M model, "q4_K weight x
- * f32 grad", q8_0 weights in the gate test -- but not their bytes; the
- * layouts below are the GGUF block formats as publicly documented):
- *   q8_0, 34 bytes / 32 values: bytes 0-1 fp16 d; bytes 2..33 int8 q[32].
- *   q4_K, 144 bytes / 256 values: bytes 0-1 fp16 d, 2-3 fp16 dmin,
+ * f32 grad", q8_0 weights in the gate test, and the MUL_MAT_ID_BACK page's
+ * list of the frozen-weight types out_prod reads: f32, f16, bf16, q4_0,
+ * q4_1, q5_0, q5_1, q8_0, q2_K..q6_K -- but not their bytes; the layouts
+ * below are the GGUF block formats as publicly documented, multi-byte
+ * fields little-endian):
+ *   f16 / bf16, 2 bytes / 1 value: IEEE binary16 / the top half of a binary32.
+ *   q4_0, 18 bytes / 32: fp16 d; 16 bytes of 4-bit q; value = d*(q-8).
+ *   q4_1, 20 bytes / 32: fp16 d, fp16 m; 16 bytes of 4-bit q; value = d*q + m.
+ *   q5_0, 22 bytes / 32: fp16 d; 32 high bits; 16 bytes of low nibbles;
+ *     value = d*(q-16).
+ *   q5_1, 24 bytes / 32: fp16 d, fp16 m; 32 high bits; 16 bytes of low
+ *     nibbles; value = d*q + m.
+ *   q8_0, 34 bytes / 32: fp16 d; bytes 2..33 int8 q[32]; value = d*q.
+ *   q2_K, 84 bytes / 256: 16 bytes of (4-bit scale, 4-bit min) for 16
+ *     sub-blocks of 16; 64 bytes of 2-bit q; fp16 d; fp16 dmin;
+ *     value = d*scale*q - dmin*min.
+ *   q3_K, 110 bytes / 256: 32 bytes of high bits; 64 bytes of 2-bit low
+ *     parts; 12 bytes of 6-bit scales for 16 sub-blocks; fp16 d;
+ *     value = d*(scale-32)*q with q in [-4, 3].
+ *   q4_K, 144 bytes / 256: bytes 0-1 fp16 d, 2-3 fp16 dmin,
  *     4..15 twelve bytes of packed 6-bit (scale, min) for 8 sub-blocks of 32,
- *     16..143 128 bytes of 4-bit q.  See q4k_subblock_params and
- *     decode_q4_K_row for the exact bit positions.
+ *     16..143 128 bytes of 4-bit q; value = d*scale*q - dmin*min.
+ *   q5_K, 176 bytes / 256: as q4_K plus 32 bytes of high bits before the
+ *     nibbles; q has 5 bits.
+ *   q6_K, 210 bytes / 256: 128 bytes of low nibbles; 64 bytes of 2-bit high
+ *     parts; 16 int8 scales for sub-blocks of 16; fp16 d;
+ *     value = d*scale*(q-32).
+ * The decoders below state the exact bit positions.  Every value is the
+ * exact block formula rounded once to float (for q3_K and the 32-value
+ * types without an offset the formula is exact in float already).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -46,8 +69,18 @@
 #endif
 
 #define ORC_F32 0
+#define ORC_F16 1
+#define ORC_Q4_0 2
+#define ORC_Q4_1 3
+#define ORC_Q5_0 6
+#define ORC_Q5_1 7
 #define ORC_Q8_0 8
+#define ORC_Q2_K 10
+#define ORC_Q3_K 11
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
+#define ORC_Q6_K 14
+#define ORC_BF16 30
 
 #define ORC_OK 0
 #define ORC_E_ARG (-1)
@@ -141,16 +174,198 @@ static int decode_q4_K_row(const uint8_t *row, int64_t n, float *out)
     return ORC_OK;
 }
 
+/* bfloat16 bits -> double: the 16 bits are the top half of a binary32, so
+ * the value is that float's.  Inf and NaN are refused (returns -1). */
+static int bf16_to_double(uint16_t h, double *out)
+{
+    if (((h >> 7) & 0xFF) == 0xFF)
+        return -1;
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    *out = (double)f;
+    return 0;
+}
+
+/* f16 and bf16 rows: one 2-byte value per element. */
+static int decode_f16_row(const uint8_t *row, int64_t n, int bf16, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double v;
+        uint16_t h = load_u16le(row + 2 * i);
+        if (bf16 ? bf16_to_double(h, &v) : half_to_double(h, &v))
+            return ORC_E_FP16;
+        out[i] = (float)v;
+    }
+    return ORC_OK;
+}
+
+/* The 32-value types.  Value j of a block (j < 16: the low nibble of code
+ * byte j; j >= 16: the high nibble of code byte j-16); q5_0 / q5_1 add bit j
+ * of the 32-bit high-bit word as bit 4 of q.  Offsets of the fields:
+ *   q4_0: d 0, codes 2        q4_1: d 0, m 2, codes 4
+ *   q5_0: d 0, high 2, codes 6  q5_1: d 0, m 2, high 4, codes 8 */
+static int decode_small_row(const uint8_t *row, int64_t n, int type, float *out)
+{
+    const int bytes = type == ORC_Q4_0 ? 18 : type == ORC_Q4_1 ? 20 : type == ORC_Q5_0 ? 22 : 24;
+    const int has_m = type == ORC_Q4_1 || type == ORC_Q5_1;
+    const int five = type == ORC_Q5_0 || type == ORC_Q5_1;
+    const int off_high = has_m ? 4 : 2;
+    const int off_codes = (has_m ? 4 : 2) + (five ? 4 : 0);
+    for (int64_t blk = 0; blk < n / 32; ++blk) {
+        const uint8_t *p = row + (int64_t)bytes * blk;
+        double d, m = 0.0;
+        if (half_to_double(load_u16le(p), &d))
+            return ORC_E_FP16;
+        if (has_m && half_to_double(load_u16le(p + 2), &m))
+            return ORC_E_FP16;
+        uint32_t high = 0;
+        if (five)
+            high = (uint32_t)p[off_high] | ((uint32_t)p[off_high + 1] << 8) |
+                   ((uint32_t)p[off_high + 2] << 16) | ((uint32_t)p[off_high + 3] << 24);
+        for (int j = 0; j < 32; ++j) {
+            const uint8_t byte = p[off_codes + (j % 16)];
+            int q = j < 16 ? (byte & 0x0F) : (byte >> 4);
+            if (five)
+                q |= (int)((high >> j) & 1u) << 4;
+            double exact;
+            if (has_m)
+                exact = d * (double)q + m;
+            else
+                exact = d * (double)(q - (five ? 16 : 8));
+            out[32 * blk + j] = (float)exact;
+        }
+    }
+    return ORC_OK;
+}
+
+/* q2_K (84 bytes): scales[16] at 0, codes[64] at 16, fp16 d at 80, fp16
+ * dmin at 82.  Value v = 128h + 32j + t (h < 2, j < 4, t < 32): q = bits
+ * 2j..2j+1 of code byte 32h + t; sub-block v/16 has scale = low nibble and
+ * min = high nibble of scales[v/16].  Value = d*scale*q - dmin*min. */
+static int decode_q2_K_row(const uint8_t *row, int64_t n, float *out)
+{
+    for (int64_t blk = 0; blk < n / 256; ++blk) {
+        const uint8_t *p = row + 84 * blk;
+        double d, dmin;
+        if (half_to_double(load_u16le(p + 80), &d) || half_to_double(load_u16le(p + 82), &dmin))
+            return ORC_E_FP16;
+        for (int v = 0; v < 256; ++v) {
+            const int h = v / 128, j = (v % 128) / 32, t = v % 32;
+            const int q = (p[16 + 32 * h + t] >> (2 * j)) & 3;
+            const int sm = p[v / 16];
+            double exact = d * (double)(sm & 0x0F) * (double)q - dmin * (double)(sm >> 4);
+            out[256 * blk + v] = (float)exact;
+        }
+    }
+    return ORC_OK;
+}
+
+/* q3_K (110 bytes): high-bit mask[32] at 0, codes[64] at 32, scales[12] at
+ * 96, fp16 d at 108.  Value v = 128h + 32j + t: low two bits = bits 2j..2j+1
+ * of code byte 32h + t; high bit = bit 4h + j of mask byte t; q = low - 4
+ * when the high bit is clear, else low.  Scale i = v/16 (6 bits, stored
+ * biased by 32): low four bits = low nibble of byte i (i < 8) or high nibble
+ * of byte i - 8 (i >= 8); top two bits = bits 2*(i/4)..+1 of byte 8 + i%4 of
+ * the scale field.  Value = d*(scale - 32)*q. */
+static int decode_q3_K_row(const uint8_t *row, int64_t n, float *out)
+{
+    for (int64_t blk = 0; blk < n / 256; ++blk) {
+        const uint8_t *p = row + 110 * blk;
+        const uint8_t *mask = p, *codes = p + 32, *sc = p + 96;
+        double d;
+        if (half_to_double(load_u16le(p + 108), &d))
+            return ORC_E_FP16;
+        for (int v = 0; v < 256; ++v) {
+            const int h = v / 128, j = (v % 128) / 32, t = v % 32;
+            const int low = (codes[32 * h + t] >> (2 * j)) & 3;
+            const int hb = (mask[t] >> (4 * h + j)) & 1;
+            const int q = hb ? low : low - 4;
+            const int i = v / 16;
+            const int lo4 = i < 8 ? (sc[i] & 0x0F) : (sc[i - 8] >> 4);
+            const int hi2 = (sc[8 + i % 4] >> (2 * (i / 4))) & 3;
+            const int scale = (lo4 | (hi2 << 4)) - 32;
+            out[256 * blk + v] = (float)(d * (double)scale * (double)q);
+        }
+    }
+    return ORC_OK;
+}
+
+/* q5_K (176 bytes): fp16 d at 0, fp16 dmin at 2, scales[12] at 4 (packed as
+ * in q4_K), high bits[32] at 16, nibbles[128] at 48.  Value v = 64g + 32s + l:
+ * the low four bits are nibble s (0: low, 1: high) of byte 32g + l; bit 4 is
+ * bit 2g + s of high-bit byte l; sub-block v/32.  Value = d*sc*q - dmin*m. */
+static int decode_q5_K_row(const uint8_t *row, int64_t n, float *out)
+{
+    for (int64_t blk = 0; blk < n / 256; ++blk) {
+        const uint8_t *p = row + 176 * blk;
+        const uint8_t *high = p + 16, *qs = p + 48;
+        double d, dmin;
+        if (half_to_double(load_u16le(p), &d) || half_to_double(load_u16le(p + 2), &dmin))
+            return ORC_E_FP16;
+        for (int v = 0; v < 256; ++v) {
+            const int g = v / 64, s = (v % 64) / 32, l = v % 32;
+            const uint8_t byte = qs[32 * g + l];
+            int q = s ? (byte >> 4) : (byte & 0x0F);
+            q |= ((high[l] >> (2 * g + s)) & 1) << 4;
+            int sc, m;
+            q4k_subblock_params(p + 4, v / 32, &sc, &m);
+            out[256 * blk + v] = (float)(d * (double)sc * (double)q - dmin * (double)m);
+        }
+    }
+    return ORC_OK;
+}
+
+/* q6_K (210 bytes): low nibbles[128] at 0, high parts[64] at 128, int8
+ * scales[16] at 192, fp16 d at 208.  Value v = 128h + 32c + l (c < 4): low
+ * four bits = nibble c/2 (0: low, 1: high) of byte 64h + 32(c%2) + l; top two
+ * bits = bits 2c..2c+1 of high byte 32h + l; q = that 6-bit number - 32;
+ * scale = scales[v/16].  Value = d*scale*q. */
+static int decode_q6_K_row(const uint8_t *row, int64_t n, float *out)
+{
+    for (int64_t blk = 0; blk < n / 256; ++blk) {
+        const uint8_t *p = row + 210 * blk;
+        const uint8_t *ql = p, *qh = p + 128;
+        const int8_t *sc = (const int8_t *)(p + 192);
+        double d;
+        if (half_to_double(load_u16le(p + 208), &d))
+            return ORC_E_FP16;
+        for (int v = 0; v < 256; ++v) {
+            const int h = v / 128, c = (v % 128) / 32, l = v % 32;
+            const uint8_t lb = ql[64 * h + 32 * (c % 2) + l];
+            const int low = c < 2 ? (lb & 0x0F) : (lb >> 4);
+            const int top = (qh[32 * h + l] >> (2 * c)) & 3;
+            const int q = (low | (top << 4)) - 32;
+            out[256 * blk + v] = (float)(d * (double)sc[v / 16] * (double)q);
+        }
+    }
+    return ORC_OK;
+}
+
 static int block_size(int a_type)
 {
-    return a_type == ORC_Q8_0 ? 32 : a_type == ORC_Q4_K ? 256 : 1;
+    switch (a_type) {
+    case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: case ORC_Q8_0: return 32;
+    case ORC_Q2_K: case ORC_Q3_K: case ORC_Q4_K: case ORC_Q5_K: case ORC_Q6_K: return 256;
+    default: return 1;
+    }
+}
+
+static int known_type(int t)
+{
+    switch (t) {
+    case ORC_F32: case ORC_F16: case ORC_BF16: case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0:
+    case ORC_Q5_1: case ORC_Q8_0: case ORC_Q2_K: case ORC_Q3_K: case ORC_Q4_K: case ORC_Q5_K:
+    case ORC_Q6_K: return 1;
+    default: return 0;
+    }
 }
 
 /* Decode nrows rows of ne00 values each.  Row r starts at byte r*row_stride. */
 int oracle_dequant_rows(const void *a, int a_type, int64_t ne00, int64_t nrows,
                         int64_t row_stride, float *out)
 {
-    if (!a || !out || ne00 < 0 || nrows < 0)
+    if (!a || !out || ne00 < 0 || nrows < 0 || !known_type(a_type))
         return ORC_E_ARG;
     if (ne00 % block_size(a_type) != 0)
         return ORC_E_SHAPE;
@@ -158,14 +373,21 @@ int oracle_dequant_rows(const void *a, int a_type, int64_t ne00, int64_t nrows,
         const uint8_t *row = (const uint8_t *)a + r * row_stride;
         float *o = out + r * ne00;
         int rc = ORC_OK;
-        if (a_type == ORC_F32)
-            memcpy(o, row, (size_t)ne00 * sizeof(float));
-        else if (a_type == ORC_Q8_0)
-            rc = decode_q8_0_row(row, ne00, o);
-        else if (a_type == ORC_Q4_K)
-            rc = decode_q4_K_row(row, ne00, o);
-        else
-            return ORC_E_ARG;
+        switch (a_type) {
+        case ORC_F32: memcpy(o, row, (size_t)ne00 * sizeof(float)); break;
+        case ORC_F16: rc = decode_f16_row(row, ne00, 0, o); break;
+        case ORC_BF16: rc = decode_f16_row(row, ne00, 1, o); break;
+        case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1:
+            rc = decode_small_row(row, ne00, a_type, o);
+            break;
+        case ORC_Q8_0: rc = decode_q8_0_row(row, ne00, o); break;
+        case ORC_Q2_K: rc = decode_q2_K_row(row, ne00, o); break;
+        case ORC_Q3_K: rc = decode_q3_K_row(row, ne00, o); break;
+        case ORC_Q4_K: rc = decode_q4_K_row(row, ne00, o); break;
+        case ORC_Q5_K: rc = decode_q5_K_row(row, ne00, o); break;
+        case ORC_Q6_K: rc = decode_q6_K_row(row, ne00, o); break;
+        default: return ORC_E_ARG;
+        }
         if (rc)
             return rc;
     }
@@ -197,7 +419,7 @@ int oracle_out_prod(const void *a, int a_type, const float *b,
         return ORC_E_SHAPE;
     if (ne02 < 1 || ne03 < 1 || ne12 % ne02 != 0 || ne13 % ne03 != 0)
         return ORC_E_SHAPE;
-    if (a_type != ORC_F32 && a_type != ORC_Q8_0 && a_type != ORC_Q4_K)
+    if (!known_type(a_type))
         return ORC_E_ARG;
     if (ne00 % block_size(a_type) != 0)
         return ORC_E_SHAPE;

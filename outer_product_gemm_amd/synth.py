@@ -26,10 +26,27 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, Q8_0, Q4_K = 0, 8, 12
-TYPE_NAMES = {F32: "f32", Q8_0: "q8_0", Q4_K: "q4_K"}
-BLOCK_VALUES = {F32: 1, Q8_0: 32, Q4_K: 256}
-BLOCK_BYTES = {F32: 4, Q8_0: 34, Q4_K: 144}
+# GGUF type ids of the a (src0) storage types
+F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0 = 0, 1, 2, 3, 6, 7, 8
+Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 10, 11, 12, 13, 14, 30
+TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q4_0: "q4_0", Q4_1: "q4_1", Q5_0: "q5_0",
+              Q5_1: "q5_1", Q8_0: "q8_0", Q2_K: "q2_K", Q3_K: "q3_K", Q4_K: "q4_K",
+              Q5_K: "q5_K", Q6_K: "q6_K"}
+BLOCK_VALUES = {F32: 1, F16: 1, BF16: 1, Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32,
+                Q2_K: 256, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {F32: 4, F16: 2, BF16: 2, Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34,
+               Q2_K: 84, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+QUANT_TYPES = (Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K)
+# Byte offsets of a block's fp16 fields: (offset, role) with role "scale" (a
+# positive multiplier, d or dmin) or "offset" (q4_1 / q5_1's additive m).
+# Every other byte of a block (codes, packed sub-block scales, high bits) is
+# drawn uniform, so each of those fields is uniform over its range.
+HALF_FIELDS = {
+    Q4_0: ((0, "scale"),), Q4_1: ((0, "scale"), (2, "offset")), Q5_0: ((0, "scale"),),
+    Q5_1: ((0, "scale"), (2, "offset")), Q8_0: ((0, "scale"),),
+    Q2_K: ((80, "scale"), (82, "scale")), Q3_K: ((108, "scale"),),
+    Q4_K: ((0, "scale"), (2, "scale")), Q5_K: ((0, "scale"), (2, "scale")), Q6_K: ((208, "scale"),),
+}
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -124,12 +141,38 @@ def q4_K_rows(rng, nrows: int, ne00: int, d_range=(1e-3, 1e-2), d_bits=None,
     return out.reshape(nrows, nblk * 144)
 
 
+def block_rows(rng, a_type: int, nrows: int, ne00: int, d_range=(1e-3, 1e-2),
+               m_range=(-0.1, 0.0)) -> np.ndarray:
+    """(nrows, row_bytes) uint8 rows of any block type: uniform random bytes,
+    then every fp16 field set to fp16(U(d_range)) (scales) or fp16(U(m_range))
+    (q4_1 / q5_1 offsets)."""
+    nblk = ne00 // BLOCK_VALUES[a_type]
+    bb = BLOCK_BYTES[a_type]
+    out = rng.integers(0, 256, size=(nrows, nblk, bb), dtype=np.uint8)
+    for off, role in HALF_FIELDS[a_type]:
+        lo, hi = d_range if role == "scale" else m_range
+        h = fp16_bits(rng.uniform(lo, hi, size=(nrows, nblk)))
+        out[:, :, off:off + 2] = h.reshape(nrows, nblk, 1).view(np.uint8).reshape(nrows, nblk, 2)
+    return out.reshape(nrows, nblk * bb)
+
+
 def quant_rows(rng, a_type: int, nrows: int, ne00: int, **kw) -> np.ndarray:
     if a_type == Q8_0:
         return q8_0_rows(rng, nrows, ne00, **kw)
     if a_type == Q4_K:
         return q4_K_rows(rng, nrows, ne00, **kw)
+    if a_type in QUANT_TYPES:
+        return block_rows(rng, a_type, nrows, ne00, **kw)
     raise ValueError("not a quantized type: %r" % a_type)
+
+
+def half_rows(rng, a_type: int, shape, std: float = 1.0) -> np.ndarray:
+    """uint16 f16 or bf16 patterns of N(0, std) values: f16 by numpy's
+    round-to-nearest conversion, bf16 as the top half of the float32 bits."""
+    x = normal_f32(rng, shape, std)
+    if a_type == F16:
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
 @dataclass
@@ -137,7 +180,8 @@ class Instance:
     """One OUT_PROD problem: host buffers plus the ggml ne/nb that address them."""
     name: str
     a_type: int
-    a: np.ndarray          # f32 (ne03, ne02, K, ne00) or uint8 (ne03, ne02, K, row_bytes)
+    a: np.ndarray          # f32 / uint16 (f16, bf16) (ne03, ne02, K, ne00), or uint8
+                           # (ne03, ne02, K, row_bytes) for block types
     b: np.ndarray          # f32 (ne13, ne12, K, ne10)
     ne: list
     nb: list
@@ -164,6 +208,8 @@ def make_instance(name: str, a_type: int, a_ne, b_ne, seed: int, a_std: float = 
     rng = rng_for(seed)
     if a_type == F32:
         a = normal_f32(rng, (ne03, ne02, K, ne00), a_std)
+    elif a_type in (F16, BF16):
+        a = half_rows(rng, a_type, (ne03, ne02, K, ne00), a_std)
     else:
         a = quant_rows(rng, a_type, ne03 * ne02 * K, ne00).reshape(ne03, ne02, K, -1)
     if b_kind == "normal":
@@ -224,6 +270,19 @@ def lora_linear_backward(prefix: str, n_in: int, n_out: int, rank: int, tokens: 
                           "input gradient through A", True),
     }
 
+
+# Every a type at the 27B up-projection shape (m 5120, k 17408, n 1024): the
+# frozen-weight types out_prod reads (pages: the MUL_MAT_ID_BACK page's list,
+# "out_prod's set").
+TYPE_SWEEP = {}
+for _t in (F32, F16, BF16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K):
+    if _t == Q4_K:
+        TYPE_SWEEP["q4_K_5120x17408"] = WORKLOADS["q4_K_5120x17408"]
+        continue
+    TYPE_SWEEP["%s_5120x17408" % TYPE_NAMES[_t]] = (
+        _t, (5120, 17408, 1, 1), (1024, 17408, 1, 1), 80 + _t, 0.02 if _t in (F32, F16, BF16) else 1.0,
+        "normal", "%s weight x f32 gradient, m 5120 k 17408 n 1024" % TYPE_NAMES[_t])
+WORKLOADS.update(TYPE_SWEEP)
 
 LORA_BACKWARD = {
     "lora_4B_linear_backward": lora_linear_backward("lora4B", 2560, 9216, 8, 512, 61),

@@ -2,8 +2,11 @@
 
 Each test names what fixes the expected value: a hand-built golden block, a
 closed form, exact rational brute force, a library routine (numpy's fp16
-conversion, float64 matmul), integer arithmetic, or an invariant of the
-definition.  Runs on the CPU only.
+conversion, torch's bfloat16 conversion, float64 matmul), integer arithmetic,
+or an invariant of the definition.  Block decoders are checked against
+test-side packers that write the fields into bytes (tests/quant_pack.py), so
+a decoder reading a bit from the wrong place disagrees with the chosen
+fields.  Runs on the CPU only.
 """
 import os
 from fractions import Fraction
@@ -130,6 +133,171 @@ def test_q4_K_single_field_isolation():
                     assert x[e] == -(37 + j)
 
 
+def _rand_half(rng, t):
+    """fp16 bits: every 4th draw subnormal or zero, else any finite pattern."""
+    if t % 4 == 0:
+        return int(rng.integers(0, 0x0400)) | (int(rng.integers(0, 2)) << 15)
+    return int(rng.integers(0, 0x7C00)) | (int(rng.integers(0, 2)) << 15)
+
+
+def _decode(blk, a_type):
+    bv, bb = oracle.BLOCK_VALUES[a_type], oracle.BLOCK_BYTES[a_type]
+    raw = np.frombuffer(blk, dtype=np.uint8)
+    n = raw.size // bb
+    return oracle.dequant_rows(raw, a_type, bv * n, 1, raw.size)[0]
+
+
+def _same(x, expect):
+    """Equal as numbers: exact for every nonzero value; a zero may carry
+    either sign (a negative scale times a zero code is -0.0), which no sum
+    can tell apart."""
+    assert np.all(np.isfinite(x)) and np.array_equal(x, expect)
+
+
+def test_f16_row_matches_numpy_conversion():
+    """f16 a: every finite binary16 pattern decodes as numpy's float16 -> float32."""
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = bits[((bits >> 10) & 0x1F) != 0x1F]
+    x = oracle.dequant_rows(finite.view(np.uint8), oracle.F16, finite.size, 1, 2 * finite.size)[0]
+    _same(x, finite.view(np.float16).astype(np.float32))
+
+
+def test_bf16_row_matches_torch_conversion():
+    """bf16 a: every finite bfloat16 pattern decodes as torch's bfloat16 -> float32."""
+    import torch
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = bits[((bits >> 7) & 0xFF) != 0xFF]
+    x = oracle.dequant_rows(finite.view(np.uint8), oracle.BF16, finite.size, 1, 2 * finite.size)[0]
+    ref = torch.from_numpy(finite.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    _same(x, ref)
+
+
+@pytest.mark.parametrize("a_type,bad", [(oracle.F16, 0x7C00), (oracle.F16, 0xFE00),
+                                        (oracle.BF16, 0x7F80), (oracle.BF16, 0xFFC1)])
+def test_f16_bf16_refuse_inf_nan(a_type, bad):
+    raw = np.array([0x3C00, bad], dtype=np.uint16).view(np.uint8)
+    with pytest.raises(ValueError):
+        oracle.dequant_rows(raw, a_type, 2, 1, 4)
+
+
+SMALL_TYPES = {
+    oracle.Q4_0: (lambda r, t: [_rand_half(r, t)], 16, qp.pack_q4_0, qp.q4_0_values),
+    oracle.Q4_1: (lambda r, t: [_rand_half(r, t), _rand_half(r, t + 1)], 16, qp.pack_q4_1,
+                  qp.q4_1_values),
+    oracle.Q5_0: (lambda r, t: [_rand_half(r, t)], 32, qp.pack_q5_0, qp.q5_0_values),
+    oracle.Q5_1: (lambda r, t: [_rand_half(r, t), _rand_half(r, t + 1)], 32, qp.pack_q5_1,
+                  qp.q5_1_values),
+}
+
+
+@pytest.mark.parametrize("a_type", list(SMALL_TYPES))
+def test_32_value_types_random_blocks_exact(a_type):
+    """q4_0 / q4_1 / q5_0 / q5_1 from packed fields (random scales incl.
+    subnormal, random codes): the exact formula rounded once to float."""
+    hdr, qmax, pack, values = SMALL_TYPES[a_type]
+    rng = np.random.default_rng(200 + a_type)
+    for t in range(40):
+        h = hdr(rng, t)
+        q = [int(x) for x in rng.integers(0, qmax, size=32)]
+        x = _decode(pack(*h, q), a_type)
+        _same(x, qp.to_f32(values(*h, q)))
+
+
+def test_q2_K_random_blocks_exact():
+    rng = np.random.default_rng(210)
+    for t in range(40):
+        d, dm = _rand_half(rng, t), _rand_half(rng, t + 2)
+        sc, mn = rng.integers(0, 16, size=16), rng.integers(0, 16, size=16)
+        q = rng.integers(0, 4, size=256)
+        _same(_decode(qp.pack_q2_K(d, dm, sc, mn, q), oracle.Q2_K),
+              qp.to_f32(qp.q2_K_values(d, dm, sc, mn, q)))
+
+
+def test_q3_K_random_blocks_exact():
+    rng = np.random.default_rng(211)
+    for t in range(40):
+        d = _rand_half(rng, t)
+        s6 = rng.integers(0, 64, size=16)
+        q = rng.integers(-4, 4, size=256)
+        _same(_decode(qp.pack_q3_K(d, s6, q), oracle.Q3_K), qp.to_f32(qp.q3_K_values(d, s6, q)))
+
+
+def test_q5_K_random_blocks_exact():
+    rng = np.random.default_rng(212)
+    for t in range(40):
+        d, dm = _rand_half(rng, t), _rand_half(rng, t + 3)
+        sc, m = rng.integers(0, 64, size=8), rng.integers(0, 64, size=8)
+        q = rng.integers(0, 32, size=256)
+        _same(_decode(qp.pack_q5_K(d, dm, sc, m, q), oracle.Q5_K),
+              qp.to_f32(qp.q5_K_values(d, dm, sc, m, q)))
+
+
+def test_q6_K_random_blocks_exact():
+    """q6_K: d*scale*q can need 25 significant bits, so the single rounding
+    to float is exercised; expected = the exact product rounded once."""
+    rng = np.random.default_rng(213)
+    for t in range(40):
+        d = _rand_half(rng, t)
+        sc = rng.integers(-128, 128, size=16)
+        q = rng.integers(-32, 32, size=256)
+        _same(_decode(qp.pack_q6_K(d, sc, q), oracle.Q6_K), qp.to_f32(qp.q6_K_values(d, sc, q)))
+
+
+def test_k_quant_sub_block_isolation():
+    """One sub-block at a time gets a nonzero scale: only its values may
+    change (pins which scale field belongs to which values) for q2_K, q3_K,
+    q5_K and q6_K."""
+    one = qp.half_bits(1.0)
+    q2 = [(v * 5 + 1) % 4 for v in range(256)]
+    q3 = [(v * 5 + 1) % 8 - 4 for v in range(256)]
+    q5 = [(v * 7 + 3) % 32 for v in range(256)]
+    q6 = [(v * 11 + 5) % 64 - 32 for v in range(256)]
+    for i in range(16):
+        sc = [0] * 16
+        sc[i] = 9
+        x = _decode(qp.pack_q2_K(one, one, sc, [0] * 16, q2), oracle.Q2_K)
+        assert all(x[v] == (9 * q2[v] if v // 16 == i else 0) for v in range(256))
+        mn = [0] * 16
+        mn[i] = 7
+        x = _decode(qp.pack_q2_K(one, one, [0] * 16, mn, q2), oracle.Q2_K)
+        assert all(x[v] == (-7 if v // 16 == i else 0) for v in range(256))
+        s6 = [32] * 16
+        s6[i] = 32 + 29 if i % 2 else 32 - 27   # top bits set / clear in turn
+        x = _decode(qp.pack_q3_K(one, s6, q3), oracle.Q3_K)
+        assert all(x[v] == ((s6[i] - 32) * q3[v] if v // 16 == i else 0) for v in range(256))
+        s8 = [0] * 16
+        s8[i] = -100 + i
+        x = _decode(qp.pack_q6_K(one, s8, q6), oracle.Q6_K)
+        assert all(x[v] == (s8[i] * q6[v] if v // 16 == i else 0) for v in range(256))
+    for j in range(8):
+        sc = [0] * 8
+        sc[j] = 41 + j
+        x = _decode(qp.pack_q5_K(one, one, sc, [0] * 8, q5), oracle.Q5_K)
+        assert all(x[v] == ((41 + j) * q5[v] if v // 32 == j else 0) for v in range(256))
+
+
+def test_cross_type_identities():
+    """Formats that embed another: q5_1 with every high bit clear is q4_1 with
+    the same bytes after the high-bit word; q5_K with every high bit clear is
+    q4_K with the same header and nibbles; q3_K with every mask bit set and
+    stored scales 32 + s is q2_K with scales s and zero mins over the same
+    code bytes."""
+    rng = np.random.default_rng(220)
+    for t in range(10):
+        d, m = _rand_half(rng, t + 1), _rand_half(rng, t + 2)
+        q = [int(x) for x in rng.integers(0, 16, size=32)]
+        _same(_decode(qp.pack_q5_1(d, m, q), oracle.Q5_1), _decode(qp.pack_q4_1(d, m, q), oracle.Q4_1))
+        sc, mm = rng.integers(0, 64, size=8), rng.integers(0, 64, size=8)
+        q4 = rng.integers(0, 16, size=256)
+        _same(_decode(qp.pack_q5_K(d, m, sc, mm, q4), oracle.Q5_K),
+              _decode(qp.pack_q4_K(d, m, sc, mm, q4), oracle.Q4_K))
+        s = rng.integers(0, 16, size=16)
+        c = rng.integers(0, 4, size=256)
+        x3 = _decode(qp.pack_q3_K(d, [32 + int(v) for v in s], c), oracle.Q3_K)
+        x2 = _decode(qp.pack_q2_K(d, qp.half_bits(0.0), s, [0] * 16, c), oracle.Q2_K)
+        _same(x3, x2)
+
+
 # ---------------------------------------------------------------- contraction
 
 def _f32_instance(rng, ne00, K, ne02, ne03, ne10, ne12, ne13, scale=1.0):
@@ -222,26 +390,55 @@ def test_brute_force_rational_strided_views():
     _assert_close_to_exact(ref, den, exact, exact_den)
 
 
-@pytest.mark.parametrize("a_type", [oracle.Q8_0, oracle.Q4_K])
+def _packed_block(rng, a_type):
+    """(bytes, exact values) of one random block of a_type, from the packers."""
+    h = lambda: qp.half_bits(rng.uniform(1e-3, 1e-2))  # noqa: E731
+    m = lambda: qp.half_bits(rng.uniform(-0.1, 0.0))   # noqa: E731
+    if a_type == oracle.Q8_0:
+        d, q = h(), rng.integers(-127, 128, size=32)
+        return qp.pack_q8_0(d, q), qp.q8_0_values(d, q)
+    if a_type == oracle.Q4_K:
+        d, dm = h(), h()
+        sc, mm, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 16, 256)
+        return qp.pack_q4_K(d, dm, sc, mm, q), qp.q4_K_values(d, dm, sc, mm, q)
+    if a_type in (oracle.Q4_0, oracle.Q5_0):
+        d, q = h(), [int(x) for x in rng.integers(0, 16 if a_type == oracle.Q4_0 else 32, 32)]
+        pack, val = (qp.pack_q4_0, qp.q4_0_values) if a_type == oracle.Q4_0 else (qp.pack_q5_0, qp.q5_0_values)
+        return pack(d, q), val(d, q)
+    if a_type in (oracle.Q4_1, oracle.Q5_1):
+        d, mv, q = h(), m(), [int(x) for x in rng.integers(0, 16 if a_type == oracle.Q4_1 else 32, 32)]
+        pack, val = (qp.pack_q4_1, qp.q4_1_values) if a_type == oracle.Q4_1 else (qp.pack_q5_1, qp.q5_1_values)
+        return pack(d, mv, q), val(d, mv, q)
+    if a_type == oracle.Q2_K:
+        d, dm = h(), h()
+        sc, mn, q = rng.integers(0, 16, 16), rng.integers(0, 16, 16), rng.integers(0, 4, 256)
+        return qp.pack_q2_K(d, dm, sc, mn, q), qp.q2_K_values(d, dm, sc, mn, q)
+    if a_type == oracle.Q3_K:
+        d, s6, q = h(), rng.integers(0, 64, 16), rng.integers(-4, 4, 256)
+        return qp.pack_q3_K(d, s6, q), qp.q3_K_values(d, s6, q)
+    if a_type == oracle.Q5_K:
+        d, dm = h(), h()
+        sc, mm, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 32, 256)
+        return qp.pack_q5_K(d, dm, sc, mm, q), qp.q5_K_values(d, dm, sc, mm, q)
+    if a_type == oracle.Q6_K:
+        d, sc, q = h(), rng.integers(-128, 128, 16), rng.integers(-32, 32, 256)
+        return qp.pack_q6_K(d, sc, q), qp.q6_K_values(d, sc, q)
+    raise ValueError(a_type)
+
+
+@pytest.mark.parametrize("a_type", [oracle.Q4_0, oracle.Q4_1, oracle.Q5_0, oracle.Q5_1, oracle.Q8_0,
+                                    oracle.Q2_K, oracle.Q3_K, oracle.Q4_K, oracle.Q5_K, oracle.Q6_K])
 def test_brute_force_rational_quant(a_type):
     """Quantized a on a tiny shape with broadcast: expected values from the
     packed fields (exact rationals), contraction by brute force."""
     rng = np.random.default_rng(12 + a_type)
-    qk = 32 if a_type == oracle.Q8_0 else 256
+    qk = oracle.BLOCK_VALUES[a_type]
     ne00, K, ne02, ne10, ne12 = qk, 3, 2, 2, 4
     rows, vals = [], []
     for _ in range(ne02 * K):
-        if a_type == oracle.Q8_0:
-            d = qp.half_bits(rng.uniform(1e-3, 1e-2))
-            q = rng.integers(-127, 128, size=32)
-            rows.append(qp.pack_q8_0(d, q))
-            vals.append(qp.q8_0_values(d, q))
-        else:
-            d = qp.half_bits(rng.uniform(1e-3, 1e-2))
-            dm = qp.half_bits(rng.uniform(1e-3, 1e-2))
-            sc, m, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 16, 256)
-            rows.append(qp.pack_q4_K(d, dm, sc, m, q))
-            vals.append(qp.q4_K_values(d, dm, sc, m, q))
+        blk, v = _packed_block(rng, a_type)
+        rows.append(blk)
+        vals.append(v)
     a = np.frombuffer(b"".join(rows), dtype=np.uint8)
     b = rng.standard_normal((1, ne12, K, ne10)).astype(np.float32)
     ne, nb = synth.make_ne_nb(a_type, (ne00, K, ne02, 1), (ne10, K, ne12, 1))
