@@ -46,6 +46,8 @@ COMPOSITE = {
 # weight, rank 8): input gradient through W and through A, the gradient of
 # the rank-8 activation, and the two adapter gradients.
 COMPOSITE.update({name: list(group) for name, group in synth.LORA_BACKWARD.items()})
+# Every frozen-weight a type at the 27B up-projection shape, one launch each.
+COMPOSITE["a_types_5120x17408"] = list(synth.TYPE_SWEEP)
 DEFAULT_WORKLOAD = "q4_K_27B_both"
 
 # The pages' per-op float-staging times for the same q4_K x f32 shapes

@@ -12,8 +12,9 @@
  * weight is out_prod(activation, grad) and the gradient of an input is
  * out_prod(weight, grad^T).  dst has the shape {a.ne0, b.ne0, b.ne2, b.ne3};
  * a's slice dims must divide b's (grouped-head broadcast: consecutive dst
- * slices share one a slice).  a may be f32 of any width, or a frozen
- * quantized weight (q8_0, q4_K) that is dequantized to f32 in registers.
+ * slices share one a slice).  a may be f32, f16 or bf16 of any width, or a
+ * frozen quantized weight (q4_0, q4_1, q5_0, q5_1, q8_0, q2_K..q6_K) of
+ * whole blocks that is dequantized to f32 in registers.
  * b and dst are f32.  Every value is staged and accumulated in fp32; nothing
  * passes through half precision (training gradients exceed half's 65504).
  *
@@ -22,15 +23,19 @@
  *            a = [ne00, K, ne02, ne03], b = [ne10, K, ne12, ne13],
  *            dst = [ne00, ne10, ne12, ne13]
  *   nb[12] = byte strides in the same order.
- *     nb[0]: 4 for f32 a, else the block size in bytes (34 for q8_0, 144 for
- *            q4_K); nb[8] must be 4 (dst dim 0 is contiguous).
+ *     nb[0]: the element or block size of a in bytes (4 for f32, 2 for f16
+ *            and bf16, 34 for q8_0, 144 for q4_K, ...: see the type list);
+ *            nb[8] must be 4 (dst dim 0 is contiguous).
  *     b: either nb[4] == 4 (row-major: each k selects a contiguous row of ne10
  *            floats) or nb[5] == 4 (K contiguous: a transposed view such as
  *            the grad^T that the matmul backward passes for the input gradient);
  *            the other b stride is any multiple of 4.
  *     nb[1..3], nb[5..7], nb[9..11]: any non-negative byte strides (views,
- *            padded rows, stride-0 broadcast of inputs), aligned to 4 bytes
- *            (2 for q8_0 a).  dst's dims must be ordered and must not overlap.
+ *            padded rows, stride-0 broadcast of inputs), aligned to 4 bytes;
+ *            a's strides and pointer need only 2-byte alignment for f16,
+ *            bf16 and the block types whose size is not a multiple of 4
+ *            (q4_0, q5_0, q8_0, q3_K, q6_K).  dst's dims must be ordered and
+ *            must not overlap.
  *
  * Memory and ownership: a, b and dst are DEVICE pointers owned by the caller.
  * The library keeps no pointer to them after a call returns.  A call only
@@ -76,17 +81,34 @@
 extern "C" {
 #endif
 
-/* a_type: the GGUF tensor type ids. */
-#define OUTPROD_TYPE_F32 0
-#define OUTPROD_TYPE_Q8_0 8  /* 34-byte block: fp16 d, int8 q[32]; value = d*q */
-#define OUTPROD_TYPE_Q4_K 12 /* 144-byte block of 256: fp16 d, fp16 dmin, 12 bytes of
-                                6-bit (scale, min) for 8 sub-blocks of 32, 128 bytes
-                                of 4-bit q; value = d*scale*q - dmin*min */
+/* a_type: the GGUF tensor type ids (the frozen-weight types OUT_PROD reads;
+ * pages: the MUL_MAT_ID_BACK page's list of out_prod's set).  Block layouts
+ * are the GGUF formats, multi-byte fields little-endian; every value is
+ * decoded to fp32 in registers, exactly up to one rounding of the block
+ * formula.  Bytes per block / values per block: */
+#define OUTPROD_TYPE_F32 0   /*   4 / 1 */
+#define OUTPROD_TYPE_F16 1   /*   2 / 1: IEEE binary16 */
+#define OUTPROD_TYPE_Q4_0 2  /*  18 / 32: fp16 d, 16 bytes of 4-bit q; d*(q-8) */
+#define OUTPROD_TYPE_Q4_1 3  /*  20 / 32: fp16 d, fp16 m, 16 bytes of 4-bit q; d*q + m */
+#define OUTPROD_TYPE_Q5_0 6  /*  22 / 32: fp16 d, 32 high bits, 16 bytes of nibbles; d*(q-16) */
+#define OUTPROD_TYPE_Q5_1 7  /*  24 / 32: fp16 d, fp16 m, 32 high bits, nibbles; d*q + m */
+#define OUTPROD_TYPE_Q8_0 8  /*  34 / 32: fp16 d, int8 q[32]; d*q */
+#define OUTPROD_TYPE_Q2_K 10 /*  84 / 256: 16 (scale, min) nibble pairs, 2-bit q, fp16 d,
+                                 fp16 dmin; d*scale*q - dmin*min */
+#define OUTPROD_TYPE_Q3_K 11 /* 110 / 256: high-bit mask, 2-bit low parts, 16 6-bit scales,
+                                 fp16 d; d*(scale-32)*q, q in [-4, 3] */
+#define OUTPROD_TYPE_Q4_K 12 /* 144 / 256: fp16 d, fp16 dmin, 12 bytes of 6-bit (scale, min)
+                                 for 8 sub-blocks of 32, 128 bytes of 4-bit q;
+                                 d*scale*q - dmin*min */
+#define OUTPROD_TYPE_Q5_K 13 /* 176 / 256: as q4_K plus 32 bytes of high bits; 5-bit q */
+#define OUTPROD_TYPE_Q6_K 14 /* 210 / 256: 4-bit low parts, 2-bit high parts, 16 int8
+                                 scales, fp16 d; d*scale*(q-32) */
+#define OUTPROD_TYPE_BF16 30 /*   2 / 1: the top half of an IEEE binary32 */
 
 /* status codes */
 #define OUTPROD_OK 0
 #define OUTPROD_E_NULL (-1)      /* ne/nb NULL, or a data pointer NULL where data is read/written */
-#define OUTPROD_E_TYPE (-2)      /* a_type is not F32, Q8_0 or Q4_K */
+#define OUTPROD_E_TYPE (-2)      /* a_type is not one of the OUTPROD_TYPE_* ids */
 #define OUTPROD_E_SHAPE (-3)     /* a negative extent */
 #define OUTPROD_E_K (-4)         /* a.ne[1] != b.ne[1] */
 #define OUTPROD_E_DST_SHAPE (-5) /* dst.ne != {a.ne0, b.ne0, b.ne2, b.ne3} */

@@ -24,9 +24,13 @@ import threading
 
 import torch  # noqa: F401  (must precede loading the library; see above)
 
-F32, Q8_0, Q4_K = 0, 8, 12
-BLOCK_VALUES = {F32: 1, Q8_0: 32, Q4_K: 256}
-BLOCK_BYTES = {F32: 4, Q8_0: 34, Q4_K: 144}
+# a types (GGUF ids; include/outprod.h OUTPROD_TYPE_*)
+F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0 = 0, 1, 2, 3, 6, 7, 8
+Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 10, 11, 12, 13, 14, 30
+BLOCK_VALUES = {F32: 1, F16: 1, BF16: 1, Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32,
+                Q2_K: 256, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {F32: 4, F16: 2, BF16: 2, Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34,
+               Q2_K: 84, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 OUTPROD_OK = 0
 STATUS = {
@@ -156,8 +160,10 @@ def plan_status(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = KER
 
 def tensor_ne_nb(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tensor, a_ne0=None):
     """ggml ne/nb of torch tensors laid out (ne3, ne2, ne1, ne0) (fewer dims are
-    padded with leading 1s).  A quantized ``a`` is a uint8 tensor whose last dim
-    is the row's bytes; ``a_ne0`` gives its value count."""
+    padded with leading 1s).  An f32 / f16 / bf16 ``a`` is a tensor of that
+    dtype (or of 2-byte integers holding the bits); a block-quantized ``a`` is
+    a uint8 tensor whose last dim is the row's bytes; ``a_ne0`` gives its
+    value count."""
     def four(t):
         shape = [1] * (4 - t.dim()) + list(t.shape)
         stride = [0] * (4 - t.dim()) + list(t.stride())
@@ -165,9 +171,11 @@ def tensor_ne_nb(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tenso
     ash, ast = four(a)
     bsh, bst = four(b)
     osh, ost = four(out)
-    if a_type == F32:
+    if BLOCK_VALUES[a_type] == 1:
         a_ne = ash
-        a_nb = [4 * s for s in ast]
+        a_nb = [a.element_size() * s for s in ast]
+        if a.element_size() != BLOCK_BYTES[a_type]:
+            raise ValueError("a's element size %d does not match the type" % a.element_size())
     else:
         if a_ne0 is None:
             a_ne0 = ash[0] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]
@@ -182,12 +190,13 @@ def out_prod_tensors(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.T
                      a_ne0: int = None, kernel: int = KERNEL_AUTO, stream=None) -> torch.Tensor:
     """OUT_PROD of torch device tensors on the current (or given) stream.
 
-    a: f32 (ne03, ne02, K, ne00), or uint8 (ne03, ne02, K, row_bytes) for q8_0/q4_K;
+    a: f32 / f16 / bf16 (ne03, ne02, K, ne00), or uint8 (ne03, ne02, K, row_bytes)
+       for the block types;
     b: f32 (ne13, ne12, K, ne10); out: f32 (ne13, ne12, ne10, ne00), allocated if None.
     """
     if out is None:
         bsh = [1] * (4 - b.dim()) + list(b.shape)
-        if a_type == F32:
+        if BLOCK_VALUES[a_type] == 1:
             ne00 = a.shape[-1]
         else:
             ne00 = a_ne0 if a_ne0 is not None else a.shape[-1] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]

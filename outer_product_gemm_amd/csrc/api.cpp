@@ -23,9 +23,33 @@
 namespace outprod {
 namespace {
 
-int block_values(int t) { return t == OUTPROD_TYPE_Q8_0 ? 32 : t == OUTPROD_TYPE_Q4_K ? 256 : 1; }
-int block_bytes(int t) { return t == OUTPROD_TYPE_Q8_0 ? 34 : t == OUTPROD_TYPE_Q4_K ? 144 : 4; }
-int align_of(int t) { return t == OUTPROD_TYPE_Q8_0 ? 2 : 4; }
+// Values and bytes per block of each a type (0 bytes: unknown type).
+struct TypeInfo {
+    int values, bytes;
+};
+TypeInfo type_info(int t) {
+    switch (t) {
+    case OUTPROD_TYPE_F32: return {1, 4};
+    case OUTPROD_TYPE_F16: return {1, 2};
+    case OUTPROD_TYPE_BF16: return {1, 2};
+    case OUTPROD_TYPE_Q4_0: return {32, 18};
+    case OUTPROD_TYPE_Q4_1: return {32, 20};
+    case OUTPROD_TYPE_Q5_0: return {32, 22};
+    case OUTPROD_TYPE_Q5_1: return {32, 24};
+    case OUTPROD_TYPE_Q8_0: return {32, 34};
+    case OUTPROD_TYPE_Q2_K: return {256, 84};
+    case OUTPROD_TYPE_Q3_K: return {256, 110};
+    case OUTPROD_TYPE_Q4_K: return {256, 144};
+    case OUTPROD_TYPE_Q5_K: return {256, 176};
+    case OUTPROD_TYPE_Q6_K: return {256, 210};
+    default: return {0, 0};
+    }
+}
+int block_values(int t) { return type_info(t).values; }
+int block_bytes(int t) { return type_info(t).bytes; }
+// a's pointer and strides: 4-byte aligned when the element or block size is a
+// multiple of 4 (the kernels read such blocks with 32-bit loads), else 2
+int align_of(int t) { return block_bytes(t) % 4 == 0 ? 4 : 2; }
 
 // x*y + z for non-negative int64, false on overflow.
 bool mul_add(int64_t x, int64_t y, int64_t z, int64_t *out) {
@@ -89,8 +113,7 @@ Problem swap_operands(const Problem &p) {
 int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
                       const int64_t *ne, const int64_t *nb, int kernel, Checked *c) {
     if (!ne || !nb) return OUTPROD_E_NULL;
-    if (a_type != OUTPROD_TYPE_F32 && a_type != OUTPROD_TYPE_Q8_0 && a_type != OUTPROD_TYPE_Q4_K)
-        return OUTPROD_E_TYPE;
+    if (block_bytes(a_type) == 0) return OUTPROD_E_TYPE;
     for (int i = 0; i < 12; ++i)
         if (ne[i] < 0) return OUTPROD_E_SHAPE;
     const int64_t ne00 = ne[0], K = ne[1], ne02 = ne[2], ne03 = ne[3];
@@ -192,8 +215,10 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     p.nb1 = nb[9];
     p.nb2 = nb[10];
     p.nb3 = nb[11];
-    p.vec_a = a_type == OUTPROD_TYPE_F32 && (uintptr_t)a % 16 == 0 && nb[1] % 16 == 0 &&
-              nb[2] % 16 == 0 && nb[3] % 16 == 0;
+    // 16-byte vector loads of a's rows (f32: 4 values, f16/bf16: 8 values)
+    p.vec_a = (a_type == OUTPROD_TYPE_F32 || a_type == OUTPROD_TYPE_F16 ||
+               a_type == OUTPROD_TYPE_BF16) &&
+              (uintptr_t)a % 16 == 0 && nb[1] % 16 == 0 && nb[2] % 16 == 0 && nb[3] % 16 == 0;
     // 16-byte vector loads of b: along its contiguous dim, so the other
     // strides must keep 16-byte alignment
     p.vec_b = (uintptr_t)b % 16 == 0 && (b_rows ? nb[5] : nb[4]) % 16 == 0 && nb[6] % 16 == 0 &&
@@ -366,7 +391,7 @@ const char *out_prod_strerror(int status) {
     switch (status) {
     case OUTPROD_OK: return "success";
     case OUTPROD_E_NULL: return "NULL pointer where memory is required";
-    case OUTPROD_E_TYPE: return "unsupported a_type (expected F32, Q8_0 or Q4_K)";
+    case OUTPROD_E_TYPE: return "unsupported a_type (not one of the OUTPROD_TYPE_* ids)";
     case OUTPROD_E_SHAPE: return "negative extent";
     case OUTPROD_E_K: return "a.ne[1] != b.ne[1] (contraction length mismatch)";
     case OUTPROD_E_DST_SHAPE: return "dst shape is not {a.ne0, b.ne0, b.ne2, b.ne3}";

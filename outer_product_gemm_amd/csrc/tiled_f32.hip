@@ -1,0 +1,16 @@
+// tiled_f32.hip -- instantiations of the tiled kernel for f32 a (every tile
+// configuration, both b layouts).
+#include "tiled_impl.h"
+
+namespace outprod {
+namespace tiled {
+
+const void *tiled_kernel_f32(int a_type, int variant, bool bt) {
+    switch (a_type) {
+    case OUTPROD_TYPE_F32: return tiled_fn<OUTPROD_TYPE_F32>(variant, bt);
+    default: return nullptr;
+    }
+}
+
+}  // namespace tiled
+}  // namespace outprod

@@ -1,0 +1,17 @@
+// tiled_q45.hip -- instantiations of the tiled kernel for q5_0 and q5_1 a (every tile
+// configuration, both b layouts).
+#include "tiled_impl.h"
+
+namespace outprod {
+namespace tiled {
+
+const void *tiled_kernel_q45(int a_type, int variant, bool bt) {
+    switch (a_type) {
+    case OUTPROD_TYPE_Q5_0: return tiled_fn<OUTPROD_TYPE_Q5_0>(variant, bt);
+    case OUTPROD_TYPE_Q5_1: return tiled_fn<OUTPROD_TYPE_Q5_1>(variant, bt);
+    default: return nullptr;
+    }
+}
+
+}  // namespace tiled
+}  // namespace outprod

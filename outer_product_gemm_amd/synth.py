@@ -142,16 +142,20 @@ def q4_K_rows(rng, nrows: int, ne00: int, d_range=(1e-3, 1e-2), d_bits=None,
 
 
 def block_rows(rng, a_type: int, nrows: int, ne00: int, d_range=(1e-3, 1e-2),
-               m_range=(-0.1, 0.0)) -> np.ndarray:
+               m_range=(-0.1, 0.0), half_bits=None) -> np.ndarray:
     """(nrows, row_bytes) uint8 rows of any block type: uniform random bytes,
     then every fp16 field set to fp16(U(d_range)) (scales) or fp16(U(m_range))
-    (q4_1 / q5_1 offsets)."""
+    (q4_1 / q5_1 offsets); half_bits = {"scale": bits, "offset": bits} fixes
+    those fields to one fp16 bit pattern instead."""
     nblk = ne00 // BLOCK_VALUES[a_type]
     bb = BLOCK_BYTES[a_type]
     out = rng.integers(0, 256, size=(nrows, nblk, bb), dtype=np.uint8)
     for off, role in HALF_FIELDS[a_type]:
-        lo, hi = d_range if role == "scale" else m_range
-        h = fp16_bits(rng.uniform(lo, hi, size=(nrows, nblk)))
+        if half_bits is not None and role in half_bits:
+            h = np.full((nrows, nblk), half_bits[role], dtype=np.uint16)
+        else:
+            lo, hi = d_range if role == "scale" else m_range
+            h = fp16_bits(rng.uniform(lo, hi, size=(nrows, nblk)))
         out[:, :, off:off + 2] = h.reshape(nrows, nblk, 1).view(np.uint8).reshape(nrows, nblk, 2)
     return out.reshape(nrows, nblk * bb)
 

@@ -85,8 +85,8 @@ def test_broadcast_divisibility():
 
 def test_type_and_block_width():
     ne, nb = base()
-    assert B.STATUS[plan(1, ne, nb)] == "E_TYPE"
-    assert B.STATUS[plan(99, ne, nb)] == "E_TYPE"
+    for bad in (4, 5, 9, 15, 16, 29, 31, 99, -1):
+        assert B.STATUS[plan(bad, ne, nb)] == "E_TYPE", bad
     ne, nb = base(synth.Q8_0, a_ne=(64, 512, 1, 1))
     assert plan(synth.Q8_0, ne, nb) == 0
     ne[0] = ne[8] = 48
@@ -233,3 +233,41 @@ def test_split_k_plans():
     # split bits need a forced family; bits above 23 are refused
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_AUTO, None, 2))] == "E_KERNEL"
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=1 << 24)] == "E_KERNEL"
+
+
+ALL_TYPES = [synth.F32, synth.F16, synth.BF16, synth.Q4_0, synth.Q4_1, synth.Q5_0, synth.Q5_1,
+             synth.Q8_0, synth.Q2_K, synth.Q3_K, synth.Q4_K, synth.Q5_K, synth.Q6_K]
+
+
+@pytest.mark.parametrize("a_type", ALL_TYPES)
+def test_every_a_type_plans(a_type):
+    """Every type of the frozen-weight set is accepted with its block size as
+    nb[0] and whole blocks; widths off the block grid, a wrong nb[0], and
+    strides or pointers below the type's alignment are refused."""
+    qk, bb = synth.BLOCK_VALUES[a_type], synth.BLOCK_BYTES[a_type]
+    width = 512
+    ne, nb = base(a_type, a_ne=(width, 64, 1, 1), b_ne=(96, 64, 1, 1))
+    assert nb[0] == bb and nb[1] == width // qk * bb
+    p = B.out_prod_plan(A, a_type, BB, D, ne, nb)
+    expect = "skinny" if a_type == synth.F32 else "tiled"
+    assert p["kernel_name"] == expect and p["flops"] == 2 * width * 96 * 64
+    if qk > 1:
+        ne2 = list(ne)
+        ne2[0] = ne2[8] = width - qk // 2
+        assert B.STATUS[plan(a_type, ne2, nb)] == "E_QK"
+    nb2 = list(nb)
+    nb2[0] = bb + 2
+    assert B.STATUS[plan(a_type, ne, nb2)] == "E_LAYOUT"
+    al = 4 if bb % 4 == 0 else 2
+    nb2 = list(nb)
+    nb2[1] += al        # row stride of the type's alignment: accepted
+    assert plan(a_type, ne, nb2) == 0
+    nb2[1] += 1         # odd stride: refused
+    assert B.STATUS[plan(a_type, ne, nb2)] == "E_LAYOUT"
+    assert plan(a_type, ne, nb, a=A + al) == 0
+    if al == 4:
+        assert B.STATUS[plan(a_type, ne, nb, a=A + 2)] == "E_LAYOUT"
+    assert B.STATUS[plan(a_type, ne, nb, a=A + 1)] == "E_LAYOUT"
+    # the skinny kernel is f32 only
+    if a_type != synth.F32:
+        assert B.STATUS[plan(a_type, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"

@@ -539,3 +539,102 @@ def test_split_k_in_graph_capture():
     finally:
         torch.cuda.synchronize()
         hip.hipStreamDestroy(raw)
+
+
+# ---------------------------------------------------------------- every a type
+
+NEW_TYPES = [synth.F16, synth.BF16, synth.Q4_0, synth.Q4_1, synth.Q5_0, synth.Q5_1,
+             synth.Q2_K, synth.Q3_K, synth.Q5_K, synth.Q6_K]
+ALL_TYPES = [synth.F32, synth.Q8_0, synth.Q4_K] + NEW_TYPES
+
+
+def _type_shapes(a_type):
+    """Shapes spanning several tiles with a ragged tail and a broadcast slice
+    dim: (a_ne, b_ne) pairs."""
+    qk = synth.BLOCK_VALUES[a_type]
+    if qk == 1:
+        return [((203, 45, 2, 1), (77, 45, 4, 1)), ((300, 130, 1, 1), (290, 130, 1, 1)),
+                ((16, 9, 1, 1), (5, 9, 1, 1))]
+    if qk == 32:
+        return [((160, 33, 2, 1), (130, 33, 4, 1)), ((352, 70, 1, 1), (150, 70, 1, 1)),
+                ((32, 1, 1, 1), (7, 1, 1, 1))]
+    return [((768, 37, 1, 2), (141, 37, 1, 2)), ((512, 64, 1, 1), (130, 64, 1, 1)),
+            ((256, 1, 1, 1), (5, 1, 1, 1))]
+
+
+@pytest.mark.parametrize("a_type", ALL_TYPES)
+def test_every_type_small_ragged(a_type):
+    """Each a type: ragged and broadcast shapes, b row-major and K-contiguous,
+    unsplit and split K, and a 2-byte offset a where the type allows it."""
+    for i, (a_ne, b_ne) in enumerate(_type_shapes(a_type)):
+        for kt in (False, True):
+            inst = synth.make_instance("t%d" % a_type, a_type, a_ne, b_ne,
+                                       seed_of("types", a_type, i, kt), b_kt=kt)
+            check_case(inst, B.kernel_code(B.KERNEL_TILED) if a_type == synth.F32 else 0)
+            if a_ne[1] >= 4:
+                check_case(inst, B.kernel_code(B.KERNEL_TILED, None, 3))
+    if synth.BLOCK_BYTES[a_type] % 4 != 0:
+        a_ne, b_ne = _type_shapes(a_type)[0]
+        inst = synth.make_instance("off", a_type, a_ne, b_ne, seed_of("off", a_type))
+        gpu = G.run(inst.a, a_type, inst.b, inst.ne, inst.nb, a_off=2)
+        ref, den = oracle.out_prod(inst.a, a_type, inst.b, inst.ne, inst.nb)
+        assert oracle.check(gpu, ref, den, TOL)["ok"]
+
+
+def _integer_a(rng, a_type, nrows, ne00):
+    """a whose decoded values are integers: fp16 scales 1, q4_1/q5_1 offsets
+    -8; f16 / bf16 integer values in [-8, 8]."""
+    if a_type in (synth.F16, synth.BF16):
+        x = rng.integers(-8, 9, size=(nrows, ne00)).astype(np.float32)
+        return x.astype(np.float16).view(np.uint16) if a_type == synth.F16 else \
+            (x.view(np.uint32) >> 16).astype(np.uint16)
+    if a_type == synth.F32:
+        return rng.integers(-8, 9, size=(nrows, ne00)).astype(np.float32)
+    one = int(synth.fp16_bits([1.0])[0])
+    minus8 = int(synth.fp16_bits([-8.0])[0])
+    if a_type == synth.Q8_0:
+        return synth.q8_0_rows(rng, nrows, ne00, d_bits=one)
+    if a_type == synth.Q4_K:
+        return synth.q4_K_rows(rng, nrows, ne00, d_bits=one, dmin_bits=one)
+    return synth.block_rows(rng, a_type, nrows, ne00, half_bits={"scale": one, "offset": minus8})
+
+
+@pytest.mark.parametrize("a_type", ALL_TYPES)
+def test_every_type_integer_exact(a_type):
+    """Integer-valued a (unit fp16 scales) and b in {-1, 0, 1}: every partial
+    sum is an integer below 2^24 (|value| <= 4096 for q6_K, K = 2048), so
+    the whole dst equals the oracle bit for bit, row-major and K-contiguous b."""
+    M, K, N = 2560, 2048, 512
+    rng = synth.rng_for(seed_of("int-type", a_type))
+    a = _integer_a(rng, a_type, K, M).reshape(1, 1, K, -1)
+    b = rng.integers(-1, 2, size=(1, 1, K, N)).astype(np.float32)
+    for kt in (False, True):
+        ne, nb = synth.make_ne_nb(a_type, (M, K, 1, 1), (N, K, 1, 1), b_kt=kt)
+        bh = np.ascontiguousarray(b.transpose(0, 1, 3, 2)) if kt else b
+        G.log("int-exact", synth.TYPE_NAMES[a_type], "kt", kt)
+        gpu = G.run(a, a_type, bh, ne, nb)
+        ref, _ = oracle.out_prod(a, a_type, bh, ne, nb)
+        assert np.array_equal(gpu, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("a_type", NEW_TYPES)
+def test_every_type_dequant_bit_exact_one_hot(a_type):
+    """One-hot b copies row k of a into dst column i1: dst holds the kernel's
+    own decoded values, which must equal the oracle's decode bit for bit (as
+    values) for every row of a 2560 x 1024 weight."""
+    M, K, N = 2560, 1024, 512
+    inst = synth.make_instance("oh", a_type, (M, K, 1, 1), (N, K, 1, 1), seed_of("onehot", a_type))
+    rowb = inst.a.shape[-1] * inst.a.itemsize
+    raw = np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1)
+    expect = oracle.dequant_rows(raw, a_type, M, K, rowb)
+    a_d = G.to_dev(raw)
+    out = torch.empty((N, M), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for start in range(0, K, N):
+        rows = np.arange(start, min(K, start + N))
+        b_d = torch.zeros((K, N), dtype=torch.float32, device="cuda:0")
+        b_d[torch.from_numpy(rows).to("cuda:0"), torch.arange(rows.size, device="cuda:0")] = 1.0
+        out.fill_(float("nan"))
+        B.out_prod(a_d.data_ptr(), a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb, stream)
+        got = out[: rows.size].cpu().numpy()
+        assert np.array_equal(got, expect[rows]), (synth.TYPE_NAMES[a_type], start)
