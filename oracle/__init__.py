@@ -70,6 +70,10 @@ def _load():
             lib.oracle_dequant_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
             lib.oracle_dequant_rows.restype = ctypes.c_int
+            lib.oracle_mul_mat_id_back.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                                   ctypes.c_void_p, _I64P, _I64P, _I64P,
+                                                   ctypes.c_int64, _DBLP, _DBLP]
+            lib.oracle_mul_mat_id_back.restype = ctypes.c_int
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
             _lib = lib
@@ -131,6 +135,41 @@ def out_prod(a: np.ndarray, a_type: int, b: np.ndarray, ne, nb, cols=None):
     if rc != 0:
         raise ValueError("oracle_out_prod failed: %d" % rc)
     return ref.reshape(shape), den.reshape(shape)
+
+
+def mul_mat_id_back(as_: np.ndarray, as_type: int, g: np.ndarray, ids: np.ndarray, ne, nb,
+                    slots=None):
+    """Reference MUL_MAT_ID_BACK (the input gradient of MUL_MAT_ID through frozen
+    experts): for slot s = i + n_used*t, row c of the result is
+    sum_r expert[ids[i,t]](c, r) * g(r, i, t).  ``ne``/``nb`` (16 each) describe
+    as, g, ids and dst (see oracle.c).  Returns ``(ref, den)`` as float64 of
+    shape ``(n_tokens, n_used, ne00)``, or ``(len(slots), ne00)``."""
+    ne = _i64(ne)
+    nb = _i64(nb)
+    ne00, n_used, n_tokens = int(ne[0]), int(ne[5]), int(ne[6])
+    if slots is None:
+        n = n_used * n_tokens
+        shape = (n_tokens, n_used, ne00)
+        sl = None
+    else:
+        sl = _i64(slots).reshape(-1)
+        n = sl.size
+        shape = (n, ne00)
+    ref = np.zeros(max(1, n * ne00), dtype=np.float64)
+    den = np.zeros(max(1, n * ne00), dtype=np.float64)
+    a_c = np.ascontiguousarray(as_) if as_ is not None else None
+    g_c = np.ascontiguousarray(g) if g is not None else None
+    i_c = np.ascontiguousarray(ids) if ids is not None else None
+    rc = _load().oracle_mul_mat_id_back(
+        a_c.ctypes.data if a_c is not None and a_c.size else None, as_type,
+        g_c.ctypes.data if g_c is not None and g_c.size else None,
+        i_c.ctypes.data if i_c is not None and i_c.size else None,
+        ne.ctypes.data_as(_I64P), nb.ctypes.data_as(_I64P),
+        sl.ctypes.data_as(_I64P) if sl is not None else None, n,
+        ref.ctypes.data_as(_DBLP), den.ctypes.data_as(_DBLP))
+    if rc != 0:
+        raise ValueError("oracle_mul_mat_id_back failed: %d" % rc)
+    return ref[: n * ne00].reshape(shape), den[: n * ne00].reshape(shape)
 
 
 def check(gpu, ref, den, tol: float = 1e-5) -> dict:

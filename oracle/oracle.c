@@ -510,3 +510,112 @@ void oracle_set_num_threads(int n)
     (void)n;
 #endif
 }
+
+/*
+ * MUL_MAT_ID_BACK: the input gradient of MUL_MAT_ID through frozen experts
+ * (pages: the MUL_MAT_ID_BACK Metal-kernel page -- one writer per element of
+ * a routed slot's row, the expert's rows walked, experts dequantized from the
+ * same types as out_prod's a; its proof is the gradient check of MUL_MAT_ID).
+ *
+ * Reading (the op's CPU definition is not on the pages): MUL_MAT_ID's slot
+ * (i, t) multiplies its input row by expert e = ids[i, t], so its input
+ * gradient is, for every slot (i < n_used, t < n_tokens) and c < ne00,
+ *
+ *   ref[t][i][c] = sum_{r<K} A_e(c, r) * g(r, i, t)
+ *   den[t][i][c] = sum_{r<K} |A_e(c, r)| * |g(r, i, t)|
+ *
+ * with A_e(c, r) the dequantized value c of row r of expert e, summed in
+ * double over r ascending.  Tensors (ggml order, byte strides):
+ *   ne[0..3]  as  = {ne00, K, n_expert, 1}   nb[0] = element or block bytes
+ *   ne[4..7]  g   = {K, n_used, n_tokens, 1} nb[4] = 4 (r contiguous)
+ *   ne[8..11] ids = {n_used, n_tokens, 1, 1} int32, nb[8] = 4
+ *   ne[12..15] dst = {ne00, n_used, n_tokens, 1} (shape check only)
+ * slots: nslots slot numbers s = i + n_used*t to compute (ref/den receive
+ * ne00 doubles per listed slot), or NULL for every slot in s order.  An id
+ * outside [0, n_expert) is refused (ORC_E_ARG).
+ */
+int oracle_mul_mat_id_back(const void *as, int as_type, const float *g, const int32_t *ids,
+                           const int64_t ne[16], const int64_t nb[16], const int64_t *slots,
+                           int64_t nslots, double *ref, double *den)
+{
+    if (!ne || !nb || !ref || !den || !known_type(as_type))
+        return ORC_E_ARG;
+    for (int i = 0; i < 16; ++i)
+        if (ne[i] < 0)
+            return ORC_E_SHAPE;
+    const int64_t ne00 = ne[0], K = ne[1], n_expert = ne[2];
+    const int64_t n_used = ne[5], n_tokens = ne[6];
+    if (ne[3] != 1 || ne[4] != K || ne[7] != 1 || ne[8] != n_used || ne[9] != n_tokens ||
+        ne[10] != 1 || ne[11] != 1 || ne[12] != ne00 || ne[13] != n_used || ne[14] != n_tokens ||
+        ne[15] != 1)
+        return ORC_E_SHAPE;
+    if (ne00 % block_size(as_type) != 0 || nb[4] != 4 || nb[8] != 4)
+        return ORC_E_SHAPE;
+    const int64_t total = n_used * n_tokens;
+    if (!slots)
+        nslots = total;
+    if (nslots == 0 || ne00 == 0)
+        return ORC_OK;
+    if (!ids || (K > 0 && (!as || !g)))
+        return ORC_E_ARG;
+    for (int64_t q = 0; q < nslots; ++q) {
+        const int64_t s = slots ? slots[q] : q;
+        if (s < 0 || s >= total)
+            return ORC_E_ARG;
+        const int64_t i = s % n_used, t = s / n_used;
+        const int32_t e = *(const int32_t *)((const uint8_t *)ids + i * 4 + t * nb[9]);
+        if (e < 0 || e >= n_expert)
+            return ORC_E_ARG;
+    }
+
+    /* one expert at a time: decode its K rows, then every listed slot routed to it */
+    float *A = NULL;
+    if (K > 0) {
+        A = (float *)malloc((size_t)(K * ne00) * sizeof(float));
+        if (!A)
+            return ORC_E_NOMEM;
+    }
+    int rc = ORC_OK;
+    for (int64_t e = 0; e < n_expert && rc == ORC_OK; ++e) {
+        int used = 0;
+        for (int64_t q = 0; q < nslots && !used; ++q) {
+            const int64_t s = slots ? slots[q] : q;
+            used = *(const int32_t *)((const uint8_t *)ids + (s % n_used) * 4 + (s / n_used) * nb[9]) == e;
+        }
+        if (!used)
+            continue;
+        if (K > 0 && oracle_dequant_rows((const uint8_t *)as + e * nb[2], as_type, ne00, K, nb[1], A)) {
+            rc = ORC_E_FP16;
+            break;
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t q = 0; q < nslots; ++q) {
+            const int64_t s = slots ? slots[q] : q;
+            const int64_t i = s % n_used, t = s / n_used;
+            if (*(const int32_t *)((const uint8_t *)ids + i * 4 + t * nb[9]) != e)
+                continue;
+            double *r = ref + q * ne00;
+            double *dn = den + q * ne00;
+            for (int64_t c = 0; c < ne00; ++c) {
+                r[c] = 0.0;
+                dn[c] = 0.0;
+            }
+            const uint8_t *gcol = (const uint8_t *)g + i * nb[5] + t * nb[6];
+            for (int64_t k = 0; k < K; ++k) {
+                const double gk = (double)*(const float *)(gcol + 4 * k);
+                const double agk = fabs(gk);
+                const float *Ak = A + k * ne00;
+                for (int64_t c = 0; c < ne00; ++c) {
+                    r[c] += (double)Ak[c] * gk;
+                    dn[c] += fabs((double)Ak[c]) * agk;
+                }
+            }
+        }
+    }
+    /* K == 0: every listed slot's row is an empty sum */
+    if (K == 0)
+        for (int64_t q = 0; q < nslots * ne00; ++q)
+            ref[q] = den[q] = 0.0;
+    free(A);
+    return rc;
+}

@@ -302,3 +302,77 @@ def workload(name: str, seed: int = None) -> Instance:
     b_kt = spec[7] if len(spec) > 7 else False
     return make_instance(name, a_type, a_ne, b_ne, s if seed is None else seed, a_std, b_kind, note,
                          b_kt=b_kt)
+
+
+# ---------------------------------------------------------------- MUL_MAT_ID_BACK inputs
+
+@dataclass
+class MoeInstance:
+    """One MUL_MAT_ID_BACK problem: frozen experts, the output gradient of
+    MUL_MAT_ID, the routing ids, and the ggml ne/nb[16] of (as, g, ids, dst)."""
+    name: str
+    a_type: int
+    a: np.ndarray      # experts: f32/uint16 (n_expert, K, ne00) or uint8 (n_expert, K, row_bytes)
+    g: np.ndarray      # f32 (n_tokens, n_used, K): g[t, i, r]
+    ids: np.ndarray    # int32 (n_tokens, n_used)
+    ne: list
+    nb: list
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def dst_shape(self):
+        return (self.ne[14], self.ne[13], self.ne[12])
+
+
+def moe_ne_nb(a_type: int, ne00: int, K: int, n_expert: int, n_used: int, n_tokens: int):
+    """ne[16], nb[16] for contiguous experts, gradient, ids and dst."""
+    rb = row_bytes(a_type, ne00)
+    ne = [ne00, K, n_expert, 1, K, n_used, n_tokens, 1, n_used, n_tokens, 1, 1,
+          ne00, n_used, n_tokens, 1]
+    nb = [BLOCK_BYTES[a_type], rb, rb * K, rb * K * n_expert,
+          4, 4 * K, 4 * K * n_used, 4 * K * n_used * n_tokens,
+          4, 4 * n_used, 4 * n_used * n_tokens, 4 * n_used * n_tokens,
+          4, 4 * ne00, 4 * ne00 * n_used, 4 * ne00 * n_used * n_tokens]
+    return ne, nb
+
+
+def top_k_ids(rng, n_expert: int, n_used: int, n_tokens: int) -> np.ndarray:
+    """int32 (n_tokens, n_used): for each token, n_used distinct experts drawn
+    uniformly (the indices of the n_used largest of n_expert uniform draws)."""
+    u = rng.random((n_tokens, n_expert))
+    return np.argsort(-u, axis=1)[:, :n_used].astype(np.int32)
+
+
+def make_moe_instance(name: str, a_type: int, ne00: int, K: int, n_expert: int, n_used: int,
+                      n_tokens: int, seed: int, a_std: float = 1.0, note: str = "") -> MoeInstance:
+    """Draw the experts, then the routing, then g from PCG64(seed)."""
+    rng = rng_for(seed)
+    if a_type == F32:
+        a = normal_f32(rng, (n_expert, K, ne00), a_std)
+    elif a_type in (F16, BF16):
+        a = half_rows(rng, a_type, (n_expert, K, ne00), a_std)
+    else:
+        a = quant_rows(rng, a_type, n_expert * K, ne00).reshape(n_expert, K, -1)
+    ids = top_k_ids(rng, n_expert, n_used, n_tokens)
+    g = normal_f32(rng, (n_tokens, n_used, K))
+    ne, nb = moe_ne_nb(a_type, ne00, K, n_expert, n_used, n_tokens)
+    return MoeInstance(name, a_type, a, g, ids, ne, nb, seed, note)
+
+
+# name -> (a_type, ne00, K, n_expert, n_used, n_tokens, seed, note).  A
+# mixture-of-experts FFN at the 4B's width (2560) with 64 q4_K experts of
+# 1024 rows, 8 routed per token, 512 tokens: the up/gate projections'
+# input gradient (ne00 = 2560, K = 1024) and the down projection's
+# (ne00 = 1024, K = 2560).
+MOE_WORKLOADS = {
+    "moe_up_back_q4_K": (Q4_K, 2560, 1024, 64, 8, 512, 91,
+                         "input gradient through 64 q4_K up-projection experts, 8 of 64 routed"),
+    "moe_down_back_q4_K": (Q4_K, 1024, 2560, 64, 8, 512, 92,
+                           "input gradient through 64 q4_K down-projection experts, 8 of 64 routed"),
+}
+
+
+def moe_workload(name: str) -> MoeInstance:
+    a_type, ne00, K, ne_e, n_used, n_tok, seed, note = MOE_WORKLOADS[name]
+    return make_moe_instance(name, a_type, ne00, K, ne_e, n_used, n_tok, seed, note=note)

@@ -581,3 +581,91 @@ def test_gate_semantics():
     assert not oracle.check(np.array([1.0, 1e-30, -2.0]), ref, den)["ok"]   # den 0 => exact 0
     assert not oracle.check(np.array([np.nan, 0.0, -2.0]), ref, den)["ok"]
     assert not oracle.check(np.array([1.0, 0.0, np.inf]), ref, den)["ok"]
+
+
+# ---------------------------------------------------------------- MUL_MAT_ID_BACK
+
+def _experts_f64(inst):
+    """Decoded experts as float64 (n_expert, K, ne00), via the pinned row decoder."""
+    ne00, K, E = inst.ne[0], inst.ne[1], inst.ne[2]
+    raw = np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1)
+    rb = inst.nb[1]
+    return oracle.dequant_rows(raw, inst.a_type, ne00, E * K, rb).reshape(E, K, ne00).astype(np.float64)
+
+
+@pytest.mark.parametrize("a_type", [oracle.F32, oracle.Q4_K, oracle.Q8_0, oracle.F16])
+def test_id_back_adjoint_of_mul_mat_id(a_type):
+    """MUL_MAT_ID_BACK is the adjoint of MUL_MAT_ID in its input: with the
+    forward written here from its definition (slot (i, t)'s output row r is
+    the dot product of expert ids[i,t]'s row r with the slot's input), the
+    pairing <forward(x), g> equals <x, back(g)> for random x and g -- the
+    gradient check the pages ran on the GPU kernel.  A transposed expert, a
+    wrong slot or expert index fails it."""
+    ne00 = 256 if a_type in (oracle.Q4_K,) else 64
+    inst = synth.make_moe_instance("adj", a_type, ne00, 40, 6, 3, 7, 300 + a_type)
+    A = _experts_f64(inst)                          # (E, K, ne00)
+    ref, _ = oracle.mul_mat_id_back(inst.a, a_type, inst.g, inst.ids, inst.ne, inst.nb)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 3, ne00))           # per-slot inputs x[t, i, c]
+    y = np.einsum("tikc,tic->tik", A[inst.ids], x)  # forward: y[t, i, r]
+    lhs = float(np.sum(y * inst.g.astype(np.float64)))
+    rhs = float(np.sum(x * ref))
+    assert abs(lhs - rhs) <= 1e-10 * (np.sum(np.abs(y * inst.g)) + 1.0)
+
+
+def test_id_back_single_expert_is_out_prod():
+    """One expert and every id 0: the result is OUT_PROD of the expert with the
+    gradient's slots as K-contiguous b columns (the matmul-backward form)."""
+    inst = synth.make_moe_instance("one", oracle.Q4_K, 512, 33, 1, 1, 10, 311)
+    assert inst.ids.shape == (10, 1) and not inst.ids.any()
+    ref, den = oracle.mul_mat_id_back(inst.a, oracle.Q4_K, inst.g, inst.ids, inst.ne, inst.nb)
+    n_slots = 10
+    ne, nb = synth.make_ne_nb(oracle.Q4_K, (512, 33, 1, 1), (n_slots, 33, 1, 1), b_kt=True)
+    r2, d2 = oracle.out_prod(inst.a, oracle.Q4_K, inst.g.reshape(n_slots, 33), ne, nb)
+    assert np.array_equal(ref.reshape(n_slots, 512), r2[0, 0])
+    assert np.array_equal(den.reshape(n_slots, 512), d2[0, 0])
+
+
+def test_id_back_expert_relabeling_invariant():
+    """Permuting the experts in memory and renaming the ids accordingly gives
+    the same result bit for bit."""
+    inst = synth.make_moe_instance("perm", oracle.Q8_0, 64, 20, 5, 2, 6, 312)
+    ref, _ = oracle.mul_mat_id_back(inst.a, inst.a_type, inst.g, inst.ids, inst.ne, inst.nb)
+    perm = np.array([3, 0, 4, 1, 2])                  # new expert j = old perm[j]
+    inv = np.argsort(perm)
+    ref2, _ = oracle.mul_mat_id_back(np.ascontiguousarray(inst.a[perm]), inst.a_type, inst.g,
+                                     inv[inst.ids].astype(np.int32), inst.ne, inst.nb)
+    assert np.array_equal(ref, ref2)
+
+
+def test_id_back_brute_force_rational():
+    """Tiny f32 case by exact rational arithmetic."""
+    inst = synth.make_moe_instance("bf", oracle.F32, 3, 4, 3, 2, 3, 313)
+    ref, den = oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, inst.ids, inst.ne, inst.nb)
+    for t in range(3):
+        for i in range(2):
+            e = inst.ids[t, i]
+            for c in range(3):
+                ex = sum(Fraction(float(inst.a[e, r, c])) * Fraction(float(inst.g[t, i, r])) for r in range(4))
+                ed = sum(abs(Fraction(float(inst.a[e, r, c])) * Fraction(float(inst.g[t, i, r]))) for r in range(4))
+                assert abs(Fraction(ref[t, i, c]) - ex) <= Fraction(1, 2 ** 45) * (ed + 1)
+                assert abs(Fraction(den[t, i, c]) - ed) <= Fraction(1, 2 ** 45) * (ed + 1)
+
+
+def test_id_back_slot_subset_and_refusals():
+    inst = synth.make_moe_instance("sub", oracle.F32, 16, 8, 4, 2, 5, 314)
+    full, _ = oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, inst.ids, inst.ne, inst.nb)
+    part, _ = oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, inst.ids, inst.ne, inst.nb,
+                                     slots=[9, 0, 4])
+    assert np.array_equal(part, full.reshape(10, 16)[[9, 0, 4]])
+    bad = inst.ids.copy()
+    bad[2, 1] = 4
+    with pytest.raises(ValueError):
+        oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, bad, inst.ne, inst.nb)
+    bad[2, 1] = -1
+    with pytest.raises(ValueError):
+        oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, bad, inst.ne, inst.nb)
+    ne = list(inst.ne)
+    ne[13] = 3   # dst n_used mismatch
+    with pytest.raises(ValueError):
+        oracle.mul_mat_id_back(inst.a, oracle.F32, inst.g, inst.ids, ne, inst.nb)
