@@ -48,6 +48,9 @@ COMPOSITE = {
 COMPOSITE.update({name: list(group) for name, group in synth.LORA_BACKWARD.items()})
 # Every frozen-weight a type at the 27B up-projection shape, one launch each.
 COMPOSITE["a_types_5120x17408"] = list(synth.TYPE_SWEEP)
+# MUL_MAT_ID_BACK through q4_K experts: the up and down projections' input
+# gradients of one mixture-of-experts FFN (64 experts, 8 routed, 512 tokens).
+COMPOSITE["moe_back_q4_K"] = list(synth.MOE_WORKLOADS)
 DEFAULT_WORKLOAD = "q4_K_27B_both"
 
 # The pages' per-op float-staging times for the same q4_K x f32 shapes
@@ -82,10 +85,25 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def is_moe(inst):
+    return isinstance(inst, synth.MoeInstance)
+
+
+def make_instance(name):
+    return synth.moe_workload(name) if name in synth.MOE_WORKLOADS else synth.workload(name)
+
+
 def algorithmic(inst):
     """flops and bytes of one launch: 2*ne00*ne10*K*slices; unique a at its
-    stored size (a broadcast a slice counts once) + b + one dst write."""
+    stored size (a broadcast a slice counts once) + b + one dst write.
+    MUL_MAT_ID_BACK: 2*ne00*K per routed slot; the experts that some slot uses
+    at their stored size + g + ids + dst."""
     ne = inst.ne
+    if is_moe(inst):
+        slots = ne[5] * ne[6]
+        used = len(np.unique(inst.ids))
+        a_bytes = synth.row_bytes(inst.a_type, ne[0]) * ne[1] * used
+        return 2 * ne[0] * ne[1] * slots, a_bytes + 4 * slots * (ne[1] + 1 + ne[0])
     slices = ne[10] * ne[11]
     flops = 2 * ne[0] * ne[4] * ne[1] * slices
     a_bytes = synth.row_bytes(inst.a_type, ne[0]) * ne[1] * ne[2] * ne[3]
@@ -100,7 +118,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    choices=sorted(list(synth.WORKLOADS) + list(COMPOSITE)))
+                    choices=sorted(list(synth.WORKLOADS) + list(synth.MOE_WORKLOADS) + list(COMPOSITE)))
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for 600 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU-oracle time for the baseline sample (0 = skip)")
@@ -127,11 +145,12 @@ def main():
     names = COMPOSITE.get(args.workload, [args.workload])
     log("workload", args.workload, names)
 
-    insts = [synth.workload(n) for n in names]
+    insts = [make_instance(n) for n in names]
     work = [algorithmic(i) for i in insts]
     flops_step = sum(w[0] for w in work)
     bytes_step = sum(w[1] for w in work)
-    set_bytes = sum(i.a.nbytes + i.b.nbytes + 4 * int(np.prod(i.dst_shape)) for i in insts)
+    set_bytes = sum(i.a.nbytes + (i.g.nbytes + i.ids.nbytes if is_moe(i) else i.b.nbytes) +
+                    4 * int(np.prod(i.dst_shape)) for i in insts)
     R = args.rotate or max(1, min(256, int(np.ceil(600e6 / set_bytes))))
 
     sets = []
@@ -139,6 +158,15 @@ def main():
         bufs = []
         for inst in insts:
             a_d = torch.from_numpy(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1)).to(dev)
+            if is_moe(inst):
+                g_d = torch.from_numpy(inst.g).to(dev)
+                i_d = torch.from_numpy(inst.ids).to(dev)
+                d_d = torch.empty(inst.dst_shape, dtype=torch.float32, device=dev)
+                plan = B.out_prod_id_back_plan(a_d.data_ptr(), inst.a_type, g_d.data_ptr(),
+                                               i_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb)
+                plan["kernel_name"] = "tiled_id"
+                bufs.append((a_d, (g_d, i_d), d_d, plan))
+                continue
             b_d = torch.from_numpy(inst.b).to(dev)
             d_d = torch.empty(inst.dst_shape, dtype=torch.float32, device=dev)
             plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(),
@@ -154,6 +182,10 @@ def main():
     def launch(r, j, stream_ptr):
         inst = insts[j]
         a_d, b_d, d_d, _ = sets[r][j]
+        if is_moe(inst):
+            B.out_prod_id_back(a_d.data_ptr(), inst.a_type, b_d[0].data_ptr(), b_d[1].data_ptr(),
+                               d_d.data_ptr(), inst.ne, inst.nb, stream_ptr)
+            return
         B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb,
                    stream_ptr)
 
@@ -283,11 +315,13 @@ def main():
         "config": {
             "workload": args.workload,
             "launches": [{"name": i.name, "a_type": synth.TYPE_NAMES[i.a_type],
-                          "ne00": i.ne[0], "K": i.ne[1], "ne10": i.ne[4],
-                          "slices": i.ne[10] * i.ne[11],
-                          "b_layout": "k_contiguous" if i.b_kt else "row",
+                          "ne00": i.ne[0], "K": i.ne[1],
+                          **({"op": "mul_mat_id_back", "n_expert": i.ne[2], "n_used": i.ne[5],
+                              "n_tokens": i.ne[6]} if is_moe(i) else
+                             {"ne10": i.ne[4], "slices": i.ne[10] * i.ne[11],
+                              "b_layout": "k_contiguous" if i.b_kt else "row"}),
                           "kernel": p[3]["kernel_name"], "variant": p[3]["variant"],
-                          "swapped": bool(p[3]["swapped"]), "us": round(u, 3)}
+                          "swapped": bool(p[3].get("swapped", 0)), "us": round(u, 3)}
                          for i, p, u in zip(insts, sets[0], launch_us)],
             "rotating_input_sets": R,
         },
@@ -336,6 +370,17 @@ def cpu_baseline(insts, sets, target_s):
         results = []
         for j, inst in enumerate(insts):
             ne = inst.ne
+            if is_moe(inst):   # sample routed slots (rows of dst)
+                n_slots = ne[5] * ne[6]
+                cnt = min(n, n_slots)
+                sl = np.sort(rng.choice(n_slots, cnt, replace=False))
+                t = time.perf_counter()
+                ref, den = oracle.mul_mat_id_back(inst.a, inst.a_type, inst.g, inst.ids, ne,
+                                                  inst.nb, slots=sl)
+                t_all += time.perf_counter() - t
+                f_all += 2 * ne[0] * ne[1] * cnt
+                results.append((j, sl, ref, den))
+                continue
             slices = ne[10] * ne[11]
             cnt = min(n, ne[4] * slices)
             flat = rng.choice(ne[4] * slices, cnt, replace=False)
@@ -352,9 +397,14 @@ def cpu_baseline(insts, sets, target_s):
     total_flops, total_t = f_all, t_all
     for j, cols, ref, den in results:
         d = sets[0][j][2].cpu().numpy()
-        g = np.stack([d[i3, i2, i1] for i1, i2, i3 in cols])
+        if is_moe(insts[j]):
+            nu = insts[j].ne[5]
+            g = np.stack([d[s // nu, s % nu] for s in cols])
+            sample_desc.append("%s: %d routed slots x %d" % (insts[j].name, len(cols), insts[j].ne[0]))
+        else:
+            g = np.stack([d[i3, i2, i1] for i1, i2, i3 in cols])
+            sample_desc.append("%s: %d dst columns x %d" % (insts[j].name, len(cols), insts[j].ne[0]))
         worst = max(worst, oracle.check(g, ref, den)["max_ratio"])
-        sample_desc.append("%s: %d dst columns x %d" % (insts[j].name, len(cols), insts[j].ne[0]))
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:

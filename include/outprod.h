@@ -194,6 +194,52 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);
 
+/*
+ * out_prod_id_back: MUL_MAT_ID_BACK, the input gradient of MUL_MAT_ID through
+ * frozen experts (pages: the MUL_MAT_ID_BACK Metal-kernel page: one writer per
+ * element of a routed slot's row, the expert's rows walked, every type of
+ * out_prod's a decoded in registers).  For every routed slot (i, t), i <
+ * n_used, t < n_tokens, with e = ids[i, t]:
+ *
+ *   dst[c, i, t] = sum_{r<K} as[c, r, e] * g[r, i, t]        (c < ne00)
+ *
+ * i.e. the slot's gradient row times expert e, each expert stored as OUT_PROD
+ * stores a (K rows of ne00 values).  dst is per slot; where the forward
+ * broadcast one input row to all used experts the caller sums dst over i.
+ *
+ * ne[16] / nb[16] (ggml order, byte strides), in this order:
+ *   as  {ne00, K, n_expert, 1}   nb[0] = element or block bytes of as_type
+ *   g   {K, n_used, n_tokens, 1} nb[4] = 4 (K contiguous, f32)
+ *   ids {n_used, n_tokens, 1, 1} nb[8] = 4 (int32)
+ *   dst {ne00, n_used, n_tokens, 1} nb[12] = 4; rows ordered and disjoint
+ * Alignment as for out_prod (a's rules for as; 4 bytes elsewhere).  At most
+ * 512 experts.  All pointers are device pointers owned by the caller.
+ *
+ * The slots are grouped by expert on the device (three small routing kernels,
+ * tables in the stream's workspace -- see "Split K and the workspace" above,
+ * including OUTPROD_E_CAPTURE), then one tiled launch runs every expert's
+ * slots; 4 launches on `stream`.  A slot whose id is outside [0, n_expert) gets
+ * a row of NaN (ids are device data; there is no host-side check).  K == 0
+ * writes zeros without reading ids; no slots or ne00 == 0: no work.
+ * Deterministic: slots keep their order within an expert and each dst row has
+ * one writer.  Returns OUTPROD_OK or a status (checks as for out_prod).
+ */
+int out_prod_id_back(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
+                     const int64_t ne[16], const int64_t nb[16], void *stream);
+
+/* out_prod_id_back with a forced tile configuration: kernel = OUTPROD_KERNEL_TILED
+ * | (index + 1) << 8 with an index the grouped kernel is built for (0, 1, 2, 4),
+ * or OUTPROD_KERNEL_AUTO. */
+int out_prod_id_back_ex(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
+                        const int64_t ne[16], const int64_t nb[16], void *stream, int kernel);
+
+/* Every check of out_prod_id_back and the launch it would make (host only):
+ * tile sizes, the grid's upper bound (tiles beyond the routed slots' needs exit
+ * at once), slots in `slices`, flops, and the workspace bytes. */
+int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int32_t *ids,
+                          const float *dst, const int64_t ne[16], const int64_t nb[16], int kernel,
+                          outprod_plan *plan);
+
 /* A static English description of a status code; never NULL. */
 const char *out_prod_strerror(int status);
 

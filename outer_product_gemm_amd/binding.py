@@ -5,6 +5,7 @@ The names follow the C ABI in ``include/outprod.h``:
 * :func:`out_prod` / :func:`out_prod_ex` take raw device addresses (ints), the
   ``ne``/``nb`` arrays and a ``hipStream_t`` address, exactly like the C calls;
 * :func:`out_prod_plan` runs the host-side checks and reports the launch;
+* :func:`out_prod_id_back` / :func:`out_prod_id_back_plan`: MUL_MAT_ID_BACK;
 * :func:`out_prod_strerror` / :func:`out_prod_version`.
 
 :func:`out_prod_tensors` is a convenience that reads ``ne``/``nb`` off torch
@@ -52,7 +53,9 @@ def kernel_code(family: int, config: int = None, splits: int = None) -> int:
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
 
 # Every symbol the header declares.
-EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_strerror", "out_prod_version")
+EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_id_back", "out_prod_id_back_ex",
+           "out_prod_id_back_plan", "out_prod_strerror", "out_prod_version")
+_I64x16 = ctypes.c_int64 * 16
 
 
 class OutProdError(RuntimeError):
@@ -92,6 +95,14 @@ def load_library(path: str = LIB_PATH):
             lib.out_prod_plan.argtypes = [vp, ctypes.c_int, vp, vp, i64p, i64p, ctypes.c_int,
                                           ctypes.POINTER(outprod_plan)]
             lib.out_prod_plan.restype = ctypes.c_int
+            lib.out_prod_id_back.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64p, i64p, vp]
+            lib.out_prod_id_back.restype = ctypes.c_int
+            lib.out_prod_id_back_ex.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64p, i64p, vp,
+                                                ctypes.c_int]
+            lib.out_prod_id_back_ex.restype = ctypes.c_int
+            lib.out_prod_id_back_plan.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64p, i64p,
+                                                  ctypes.c_int, ctypes.POINTER(outprod_plan)]
+            lib.out_prod_id_back_plan.restype = ctypes.c_int
             lib.out_prod_strerror.argtypes = [ctypes.c_int]
             lib.out_prod_strerror.restype = ctypes.c_char_p
             lib.out_prod_version.restype = ctypes.c_int
@@ -104,6 +115,13 @@ def _arr12(x):
     if len(vals) != 12:
         raise ValueError("ne/nb must have 12 entries")
     return _I64x12(*vals)
+
+
+def _arr16(x):
+    vals = [int(v) for v in x]
+    if len(vals) != 16:
+        raise ValueError("ne/nb must have 16 entries")
+    return _I64x16(*vals)
 
 
 def _check(status: int) -> None:
@@ -147,6 +165,43 @@ def out_prod_plan(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = K
     d = {name: getattr(p, name) for name, _ in outprod_plan._fields_}
     d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
     return d
+
+
+def out_prod_id_back(as_: int, as_type: int, g: int, ids: int, dst: int, ne, nb,
+                     stream: int = 0) -> None:
+    """C ``out_prod_id_back`` (MUL_MAT_ID_BACK) on raw device addresses; ne/nb have
+    16 entries (as, g, ids, dst).  Raises OutProdError on a non-zero status."""
+    _check(load_library().out_prod_id_back(as_ or None, int(as_type), g or None, ids or None,
+                                           dst or None, _arr16(ne), _arr16(nb), stream or None))
+
+
+def out_prod_id_back_status(as_: int, as_type: int, g: int, ids: int, dst: int, ne, nb,
+                            stream: int = 0, kernel: int = KERNEL_AUTO) -> int:
+    """``out_prod_id_back_ex`` returning the raw status instead of raising."""
+    return int(load_library().out_prod_id_back_ex(as_ or None, int(as_type), g or None, ids or None,
+                                                  dst or None, _arr16(ne), _arr16(nb),
+                                                  stream or None, int(kernel)))
+
+
+def out_prod_id_back_plan(as_: int, as_type: int, g: int, ids: int, dst: int, ne, nb,
+                          kernel: int = KERNEL_AUTO) -> dict:
+    """C ``out_prod_id_back_plan``: host-side checks and the launch a call would make."""
+    p = outprod_plan()
+    _check(load_library().out_prod_id_back_plan(as_ or None, int(as_type), g or None, ids or None,
+                                                dst or None, _arr16(ne), _arr16(nb), int(kernel),
+                                                ctypes.byref(p)))
+    d = {name: getattr(p, name) for name, _ in outprod_plan._fields_}
+    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
+    return d
+
+
+def id_back_plan_status(as_: int, as_type: int, g: int, ids: int, dst: int, ne, nb,
+                        kernel: int = KERNEL_AUTO) -> int:
+    """``out_prod_id_back_plan`` returning the raw status instead of raising."""
+    p = outprod_plan()
+    return int(load_library().out_prod_id_back_plan(as_ or None, int(as_type), g or None,
+                                                    ids or None, dst or None, _arr16(ne), _arr16(nb),
+                                                    int(kernel), ctypes.byref(p)))
 
 
 def plan_status(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = KERNEL_AUTO) -> int:

@@ -346,10 +346,195 @@ int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne
     return e == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
 }
 
+// ---------------------------------------------------------------- MUL_MAT_ID_BACK
+
+struct IdChecked {
+    IdProblem p;
+    Launch l;
+    bool zero;  // K == 0: dst rows are zeros, no routing
+};
+
+// ne/nb[16]: as {ne00, K, n_expert, 1}, g {K, n_used, n_tokens, 1}, ids
+// {n_used, n_tokens, 1, 1}, dst {ne00, n_used, n_tokens, 1}.
+int validate_id_back(const void *as, int as_type, const float *g, const int32_t *ids,
+                     const float *dst, const int64_t *ne, const int64_t *nb, int kernel,
+                     IdChecked *c) {
+    if (!ne || !nb) return OUTPROD_E_NULL;
+    if (block_bytes(as_type) == 0) return OUTPROD_E_TYPE;
+    for (int i = 0; i < 16; ++i)
+        if (ne[i] < 0) return OUTPROD_E_SHAPE;
+    const int64_t ne00 = ne[0], K = ne[1], E = ne[2], n_used = ne[5], n_tok = ne[6];
+    if (ne[4] != K) return OUTPROD_E_K;
+    if (ne[3] != 1 || ne[7] != 1 || ne[8] != n_used || ne[9] != n_tok || ne[10] != 1 || ne[11] != 1)
+        return OUTPROD_E_SHAPE;
+    if (ne[12] != ne00 || ne[13] != n_used || ne[14] != n_tok || ne[15] != 1) return OUTPROD_E_DST_SHAPE;
+
+    memset(c, 0, sizeof(*c));
+    IdProblem &p = c->p;
+    Launch &l = c->l;
+    p.a_type = as_type;
+    p.M = ne00;
+    p.K = K;
+    p.n_expert = E;
+    p.n_used = n_used;
+    p.n_tokens = n_tok;
+    const int64_t slots = n_used * n_tok;
+    if (ne00 == 0 || slots == 0) {
+        const int fam = kernel & 0xFF;
+        if (fam != OUTPROD_KERNEL_AUTO && fam != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
+        l.kernel = OUTPROD_KERNEL_NONE;
+        return OUTPROD_OK;
+    }
+    if (K > 0 && E < 1) return OUTPROD_E_BCAST;  // no expert to route to
+    if (ne00 % block_values(as_type) != 0) return OUTPROD_E_QK;
+
+    // layout: dim 0 of each tensor contiguous; 4-byte strides (2 for the
+    // experts of 2-byte aligned types); dst rows ordered and disjoint
+    if (nb[0] != block_bytes(as_type) || nb[4] != 4 || nb[8] != 4 || nb[12] != 4) return OUTPROD_E_LAYOUT;
+    for (int i = 0; i < 16; ++i)
+        if (nb[i] < 0) return OUTPROD_E_LAYOUT;
+    const int al = align_of(as_type);
+    if (nb[1] % al || nb[2] % al || nb[5] % 4 || nb[6] % 4 || nb[9] % 4 || nb[13] % 4 || nb[14] % 4)
+        return OUTPROD_E_LAYOUT;
+    if ((uintptr_t)as % al || (uintptr_t)g % 4 || (uintptr_t)ids % 4 || (uintptr_t)dst % 4)
+        return OUTPROD_E_LAYOUT;
+    if (n_used > 1 && nb[13] < 4 * ne00) return OUTPROD_E_LAYOUT;
+    if (n_tok > 1 && nb[14] < (n_used - 1) * nb[13] + 4 * ne00) return OUTPROD_E_LAYOUT;
+    if (!dst) return OUTPROD_E_NULL;
+    if (K > 0 && (!as || !g || !ids)) return OUTPROD_E_NULL;
+
+    // index range (32-bit kernel indices) and extents
+    const int64_t lim = INT32_MAX;
+    if (ne00 > lim || K > lim || slots > lim / 4 || E > kIdMaxExperts) return OUTPROD_E_RANGE;
+    const int64_t a_row = ne00 / block_values(as_type) * block_bytes(as_type);
+    int64_t ext_a = 0, ext_g = 0, ext_i = 0, ext_d = 0;
+    {
+        const int64_t dne[4] = {ne00, n_used, n_tok, 1}, dnb[4] = {4, nb[13], nb[14], nb[15]};
+        if (!extent(4 * ne00, dne, dnb, &ext_d)) return OUTPROD_E_RANGE;
+    }
+    if (K > 0) {
+        const int64_t ane[4] = {ne00, K, E, 1}, anb[4] = {nb[0], nb[1], nb[2], nb[3]};
+        const int64_t gne[4] = {K, n_used, n_tok, 1}, gnb[4] = {4, nb[5], nb[6], nb[7]};
+        const int64_t ine[4] = {n_used, n_tok, 1, 1}, inb[4] = {4, nb[9], nb[10], nb[11]};
+        if (!extent(a_row, ane, anb, &ext_a) || !extent(4 * K, gne, gnb, &ext_g) ||
+            !extent(4 * n_used, ine, inb, &ext_i))
+            return OUTPROD_E_RANGE;
+        if (overlaps(dst, ext_d, as, ext_a) || overlaps(dst, ext_d, g, ext_g) ||
+            overlaps(dst, ext_d, ids, ext_i))
+            return OUTPROD_E_ALIAS;
+    }
+
+    p.as = (const uint8_t *)as;
+    p.g = (const uint8_t *)g;
+    p.ids = (const uint8_t *)ids;
+    p.dst = (uint8_t *)dst;
+    p.nb01 = nb[1];
+    p.nb02 = nb[2];
+    p.nbg1 = nb[5];
+    p.nbg2 = nb[6];
+    p.nbi1 = nb[9];
+    p.nbd1 = nb[13];
+    p.nbd2 = nb[14];
+    p.vec_a = (as_type == OUTPROD_TYPE_F32 || as_type == OUTPROD_TYPE_F16 ||
+               as_type == OUTPROD_TYPE_BF16) &&
+              (uintptr_t)as % 16 == 0 && nb[1] % 16 == 0 && nb[2] % 16 == 0;
+    p.vec_g = (uintptr_t)g % 16 == 0 && nb[5] % 16 == 0 && nb[6] % 16 == 0;
+
+    const int fam = kernel & 0xFF, variant = (kernel >> 8) & 0xFF;
+    if ((kernel >> 16) != 0 || (fam != OUTPROD_KERNEL_AUTO && fam != OUTPROD_KERNEL_TILED))
+        return OUTPROD_E_KERNEL;
+    if (K == 0) {
+        c->zero = true;
+        l.kernel = OUTPROD_KERNEL_ZERO;
+        return OUTPROD_OK;
+    }
+    l.variant = variant;
+    if (!plan_id_back(p, &l)) return OUTPROD_E_KERNEL;
+    if (l.grid > lim || id_workspace_bytes(p) > kWorkspaceBytes) return OUTPROD_E_RANGE;
+    return OUTPROD_OK;
+}
+
+// dst rows of an ID problem as an OUT_PROD dst (for the zero kernel)
+Problem id_dst_as_problem(const IdProblem &q) {
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    p.dst = q.dst;
+    p.M = q.M;
+    p.N = q.n_used;
+    p.ne12 = q.n_tokens;
+    p.ne13 = 1;
+    p.nb0 = 4;
+    p.nb1 = q.nbd1;
+    p.nb2 = q.nbd2;
+    p.nb3 = 0;
+    p.dps2 = p.dps3 = 1;
+    return p;
+}
+
+int run_id_back(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
+                const int64_t *ne, const int64_t *nb, void *stream, int kernel) {
+    IdChecked c;
+    int rc = validate_id_back(as, as_type, g, ids, dst, ne, nb, kernel, &c);
+    if (rc != OUTPROD_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (c.l.kernel == OUTPROD_KERNEL_NONE) return OUTPROD_OK;
+    hipError_t e;
+    if (c.zero) {
+        Problem z = id_dst_as_problem(c.p);
+        Launch zl;
+        memset(&zl, 0, sizeof(zl));
+        plan_zero(z, &zl);
+        e = launch_zero(z, zl, s);
+    } else {
+        uint8_t *ws = nullptr;
+        rc = stream_workspace(s, &ws);
+        if (rc != OUTPROD_OK) return rc;
+        c.p.ws = ws;
+        e = launch_id_back(c.p, c.l, s);
+    }
+    return e == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
+}
+
 }  // namespace
 }  // namespace outprod
 
 extern "C" {
+
+int out_prod_id_back(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
+                     const int64_t ne[16], const int64_t nb[16], void *stream) {
+    return outprod::run_id_back(as, as_type, g, ids, dst, ne, nb, stream, OUTPROD_KERNEL_AUTO);
+}
+
+int out_prod_id_back_ex(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
+                        const int64_t ne[16], const int64_t nb[16], void *stream, int kernel) {
+    return outprod::run_id_back(as, as_type, g, ids, dst, ne, nb, stream, kernel);
+}
+
+int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int32_t *ids,
+                          const float *dst, const int64_t ne[16], const int64_t nb[16], int kernel,
+                          outprod_plan *plan) {
+    if (!plan) return OUTPROD_E_NULL;
+    outprod::IdChecked c;
+    int rc = outprod::validate_id_back(as, as_type, g, ids, dst, ne, nb, kernel, &c);
+    if (rc != OUTPROD_OK) return rc;
+    memset(plan, 0, sizeof(*plan));
+    plan->kernel = c.l.kernel;
+    plan->tile_m = c.l.tile_m;
+    plan->tile_n = c.l.tile_n;
+    plan->tile_k = c.l.tile_k;
+    plan->block = c.l.block;
+    plan->lds_bytes = c.l.lds_bytes;
+    plan->grid = c.l.grid;
+    plan->slices = c.p.n_used * c.p.n_tokens;
+    plan->dps2 = plan->dps3 = 1;
+    plan->flops = 2 * c.p.M * c.p.K * c.p.n_used * c.p.n_tokens;
+    plan->variant = c.l.variant;
+    plan->splits = 1;
+    plan->ksplit = c.p.K;
+    plan->workspace_bytes = c.l.kernel == OUTPROD_KERNEL_TILED ? outprod::id_workspace_bytes(c.p) : 0;
+    return OUTPROD_OK;
+}
+
 
 int out_prod(const void *a, int a_type, const float *b, float *dst, const int64_t ne[12],
              const int64_t nb[12], void *stream) {

@@ -1,0 +1,262 @@
+// kernel_id_back.hip -- MUL_MAT_ID_BACK: the input gradient of MUL_MAT_ID
+// through frozen experts, dst row (i, t) = expert ids[i,t] x g[:, i, t]
+// (pages: the MUL_MAT_ID_BACK Metal-kernel page: one writer per dst
+// element, the expert's rows walked, no expert copied or transposed, the
+// frozen-weight types of out_prod decoded in registers).
+//
+// The page runs one threadgroup per routed slot, so every slot reads its
+// expert's whole matrix.  Here the slots are grouped by expert on the device
+// and each expert runs as one OUT_PROD-shaped tile job with the slots'
+// gradient columns gathered as its b (K contiguous) -- the tiled MFMA kernel
+// reads each expert once per 64 or 128 of its slots:
+//   1. id_rank_kernel   (one block per 1024 slots) the stable rank of each
+//      slot among the block's slots of the same expert (wave ballots), and
+//      the block's per-expert counts;
+//   2. id_scan_kernel   (one block) per-block bases, per-expert offsets and
+//      the tile table (expert, first row) of BN-slot tiles;
+//   3. id_place_kernel  the expert-sorted slot list; a slot whose id is not
+//      an expert gets a NaN dst row;
+//   4. tiled_id_kernel  (tiled_impl.h) one workgroup per (tile, m-tile).
+// Slots keep their order within an expert, every dst row has one writer and
+// its sum runs over K in a fixed order: the result is deterministic.  The
+// tables live in the stream's workspace; nothing is cleared in advance (every
+// entry read is written first, in stream order).
+#include <algorithm>
+#include <cmath>
+
+#include "kernel_common.h"
+#include "outprod.h"
+#include "tiled_impl.h"
+
+namespace outprod {
+namespace {
+
+__global__ __launch_bounds__(kIdRankBlock) void id_rank_kernel(IdProblem p) {
+    constexpr int W = kIdRankBlock / 64;
+    __shared__ int wcnt[W][kIdMaxExperts];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = (int)p.n_expert, nu = (int)p.n_used;
+    const int total = (int)(p.n_used * p.n_tokens);
+    int *ws = (int *)p.ws;
+    for (int x = tid; x < W * kIdMaxExperts; x += kIdRankBlock) wcnt[x / kIdMaxExperts][x % kIdMaxExperts] = 0;
+    __syncthreads();
+
+    const int s = blockIdx.x * kIdRankBlock + tid;
+    int e = -1;
+    if (s < total) {
+        const int i = s % nu, t = s / nu;
+        const int v = *(const int *)(p.ids + (int64_t)i * 4 + (int64_t)t * p.nbi1);
+        e = (v >= 0 && v < E) ? v : -1;
+    }
+    // rank among this wave's lower lanes with the same expert: one ballot per
+    // distinct expert of the wave (wave-uniform loop)
+    int rank = 0;
+    unsigned long long todo = __ballot(e >= 0);
+    while (todo) {
+        const int leader = __ffsll((unsigned long long)todo) - 1;
+        const int le = __shfl(e, leader);
+        const unsigned long long peers = __ballot(e == le);
+        if (e == le) rank = __popcll(peers & ((1ull << lane) - 1ull));
+        if (lane == leader) wcnt[wave][le] = __popcll(peers);
+        todo &= ~peers;
+    }
+    __syncthreads();
+    // per expert: exclusive prefix over the waves; the block's count to hist
+    for (int x = tid; x < E; x += kIdRankBlock) {
+        int acc = 0;
+        for (int w = 0; w < W; ++w) {
+            const int c = wcnt[w][x];
+            wcnt[w][x] = acc;
+            acc += c;
+        }
+        ws[p.off_hist + (int64_t)blockIdx.x * E + x] = acc;
+    }
+    __syncthreads();
+    if (s < total) ws[p.off_rank + s] = e >= 0 ? wcnt[wave][e] + rank : -1;
+}
+
+__global__ __launch_bounds__(1024) void id_scan_kernel(IdProblem p) {
+    __shared__ int sc[1024], st[1024];
+    const int tid = threadIdx.x, E = (int)p.n_expert, B = p.rank_blocks;
+    int *ws = (int *)p.ws;
+    // per expert: exclusive scan over the rank blocks (hist becomes each
+    // block's base within the expert)
+    int c = 0;
+    if (tid < E) {
+        for (int b = 0; b < B; ++b) {
+            int *h = ws + p.off_hist + (int64_t)b * E + tid;
+            const int v = *h;
+            *h = c;
+            c += v;
+        }
+    }
+    const int nt = tid < E ? (c + p.bn - 1) / p.bn : 0;
+    // inclusive scans over experts of slot counts and tile counts
+    sc[tid] = c;
+    st[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a = tid >= off ? sc[tid - off] : 0;
+        const int b = tid >= off ? st[tid - off] : 0;
+        __syncthreads();
+        sc[tid] += a;
+        st[tid] += b;
+        __syncthreads();
+    }
+    if (tid < E) {
+        ws[p.off_offsets + tid] = sc[tid] - c;
+        const int t0 = st[tid] - nt;
+        for (int j = 0; j < nt; ++j) {
+            ws[p.off_tile_e + t0 + j] = tid;
+            ws[p.off_tile_r0 + t0 + j] = j * p.bn;
+        }
+    }
+    if (tid == E - 1) {
+        ws[p.off_offsets + E] = sc[tid];
+        ws[p.off_ntiles] = st[tid];
+    }
+}
+
+__global__ __launch_bounds__(256) void id_place_kernel(IdProblem p) {
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    const int total = (int)(p.n_used * p.n_tokens), nu = (int)p.n_used, E = (int)p.n_expert;
+    if (s >= total) return;
+    int *ws = (int *)p.ws;
+    const int i = s % nu, t = s / nu;
+    const int r = ws[p.off_rank + s];
+    if (r < 0) {  // id outside [0, n_expert): the row is NaN
+        float *d = (float *)(p.dst + (int64_t)i * p.nbd1 + (int64_t)t * p.nbd2);
+        for (int c = 0; c < (int)p.M; ++c) d[c] = __builtin_nanf("");
+        return;
+    }
+    const int e = *(const int *)(p.ids + (int64_t)i * 4 + (int64_t)t * p.nbi1);
+    const int blk = s / kIdRankBlock;
+    const int pos = ws[p.off_offsets + e] + ws[p.off_hist + (int64_t)blk * E + e] + r;
+    ws[p.off_sorted + pos] = s;
+}
+
+const void *id_kernel_for(int a_type, int cfg) {
+    using namespace tiled;
+    switch (a_type) {
+    case OUTPROD_TYPE_F32: return tiled_kernel_f32(a_type, cfg, false, true);
+    case OUTPROD_TYPE_F16:
+    case OUTPROD_TYPE_BF16: return tiled_kernel_half(a_type, cfg, false, true);
+    case OUTPROD_TYPE_Q8_0:
+    case OUTPROD_TYPE_Q4_0:
+    case OUTPROD_TYPE_Q4_1: return tiled_kernel_q8(a_type, cfg, false, true);
+    case OUTPROD_TYPE_Q5_0:
+    case OUTPROD_TYPE_Q5_1: return tiled_kernel_q45(a_type, cfg, false, true);
+    case OUTPROD_TYPE_Q4_K:
+    case OUTPROD_TYPE_Q2_K: return tiled_kernel_k4(a_type, cfg, false, true);
+    case OUTPROD_TYPE_Q3_K:
+    case OUTPROD_TYPE_Q5_K:
+    case OUTPROD_TYPE_Q6_K: return tiled_kernel_k(a_type, cfg, false, true);
+    default: return nullptr;
+    }
+}
+
+void set_layout(IdProblem &p, int bn) {
+    const int64_t slots = p.n_used * p.n_tokens;
+    p.bn = bn;
+    p.rank_blocks = (int)((slots + kIdRankBlock - 1) / kIdRankBlock);
+    p.max_tiles = (int)((slots + bn - 1) / bn + p.n_expert);
+    p.off_rank = 0;
+    p.off_hist = slots;
+    p.off_offsets = p.off_hist + (int64_t)p.rank_blocks * p.n_expert;
+    p.off_sorted = p.off_offsets + p.n_expert + 1;
+    p.off_tile_e = p.off_sorted + slots;
+    p.off_tile_r0 = p.off_tile_e + p.max_tiles;
+    p.off_ntiles = p.off_tile_r0 + p.max_tiles;
+}
+
+}  // namespace
+
+int64_t id_workspace_bytes(const IdProblem &p) { return 4 * (p.off_ntiles + 1); }
+
+// Expected tiles per expert with BN-slot tiles when each token routes to
+// n_used distinct experts of n_expert uniformly: an expert's slot count is
+// binomial(n_tokens, n_used/n_expert), taken here as a normal distribution
+// and summed over +-4 standard deviations.
+double expected_tiles_per_expert(const IdProblem &p, int bn) {
+    const double q = (double)p.n_used / (double)p.n_expert;
+    const double mean = (double)p.n_tokens * (q < 1.0 ? q : 1.0);
+    const double sd = std::sqrt(std::max(mean * (1.0 - (q < 1.0 ? q : 1.0)), 1e-9));
+    const int lo = std::max(0, (int)std::floor(mean - 4 * sd)), hi = (int)std::ceil(mean + 4 * sd);
+    double w_sum = 0, t_sum = 0;
+    for (int c = lo; c <= hi; ++c) {
+        const double z = (c - mean) / sd, w = std::exp(-0.5 * z * z);
+        w_sum += w;
+        t_sum += w * (double)((c + bn - 1) / bn);
+    }
+    return w_sum > 0 ? t_sum / w_sum : 1.0;
+}
+
+// Grouped-kernel configurations the automatic choice considers: 64 x 64,
+// 128 x 80 and 128 x 128 tiles (the others can be forced).
+constexpr int kIdAuto[] = {4, 12, 0};
+
+// l->variant on entry: forced configuration + 1 (an index into kCfgs that is
+// built for the grouped kernel), or 0 for automatic.  The automatic choice
+// minimizes the estimated time: workgroups x tile area x K / eff (eff as
+// for OUT_PROD), slowed in proportion when there are fewer than 640
+// workgroups (2.5 per CU: the CUs' MFMA pipes are not kept busy), with the
+// workgroup count from the expected tiles per expert.  Measured on MI355X
+// with 64 q4_K experts, 8 of 64 routed, 512 tokens: ne00 2560 x K 1024 runs
+// best with 128 x 80 tiles (1280 workgroups), ne00 1024 x K 2560 with 64 x 64
+// (1376 workgroups; 128 x 80 leaves only 512).
+bool plan_id_back(IdProblem &p, Launch *l) {
+    using namespace tiled;
+    int best = -1;
+    if (l->variant > 0) {
+        for (int i = 0; i < kNumIdCfgs; ++i)
+            if (kIdCfgs[i] == l->variant - 1) best = kIdCfgs[i];
+        if (best < 0) return false;
+    } else {
+        double best_cost = 0;
+        for (int cfg : kIdAuto) {
+            const TileCfg &c = kCfgs[cfg];
+            const double wgs = (double)((p.M + c.bm() - 1) / c.bm()) * (double)p.n_expert *
+                               expected_tiles_per_expert(p, c.bn());
+            const double fill = std::min(1.0, wgs / 640.0);
+            const double cost = wgs * c.bm() * c.bn() * (double)p.K / c.eff / fill;
+            if (best < 0 || cost < best_cost) {
+                best = cfg;
+                best_cost = cost;
+            }
+        }
+    }
+    const TileCfg &c = kCfgs[best];
+    set_layout(p, c.bn());
+    l->kernel = OUTPROD_KERNEL_TILED;
+    l->variant = best;
+    l->tile_m = c.bm();
+    l->tile_n = c.bn();
+    l->tile_k = c.bk;
+    l->block = c.threads();
+    l->lds_bytes = 2 * c.bk * (lds_ld(c.bm(), c.mf) + lds_ld(c.bn(), c.mf)) * 4 + 2 * c.bn() * 8;
+    l->grid = ((p.M + c.bm() - 1) / c.bm()) * (int64_t)p.max_tiles;
+    l->splits = 1;
+    l->ksplit = p.K;
+    return true;
+}
+
+hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s) {
+    const void *fn = id_kernel_for(p.a_type, l.variant);
+    if (!fn) return hipErrorInvalidValue;
+    IdProblem pp = p;
+    const int64_t slots = p.n_used * p.n_tokens;
+    void *args1[] = {&pp};
+    hipError_t e = hipLaunchKernel((const void *)&id_rank_kernel, dim3((unsigned)p.rank_blocks),
+                                   dim3(kIdRankBlock), args1, 0, s);
+    if (e == hipSuccess)
+        e = hipLaunchKernel((const void *)&id_scan_kernel, dim3(1), dim3(1024), args1, 0, s);
+    if (e == hipSuccess)
+        e = hipLaunchKernel((const void *)&id_place_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256),
+                            args1, 0, s);
+    if (e != hipSuccess) return e;
+    int tiles_m = (int)((p.M + l.tile_m - 1) / l.tile_m);
+    void *args[] = {&pp, &tiles_m};
+    return hipLaunchKernel(fn, dim3((unsigned)l.grid), dim3(l.block), args, 0, s);
+}
+
+}  // namespace outprod

@@ -56,6 +56,35 @@ struct Launch {
     int64_t ksplit;   // rows per split
 };
 
+// One validated MUL_MAT_ID_BACK problem: for routed slot s = i + n_used*t,
+// dst row (i, t) = expert ids[i,t] (ne00 x K, rows of ne00 values along K)
+// times the slot's gradient column g[:, i, t] (K contiguous floats).
+struct IdProblem {
+    const uint8_t *as;    // experts: row r of expert e at as + e*nb02 + r*nb01
+    const uint8_t *g;     // g(r, i, t) at g + 4r + i*nbg1 + t*nbg2
+    const uint8_t *ids;   // int32 ids[i, t] at ids + 4i + t*nbi1
+    uint8_t *dst;         // dst(c, i, t) at dst + 4c + i*nbd1 + t*nbd2
+    int a_type;
+    int64_t M, K;         // ne00, expert rows
+    int64_t n_expert, n_used, n_tokens;
+    int64_t nb01, nb02, nbg1, nbg2, nbi1, nbd1, nbd2;
+    bool vec_a, vec_g;
+    // routing tables in the workspace (int32 offsets from ws)
+    uint8_t *ws;
+    int bn;               // slots per tile of the grouped kernel
+    int rank_blocks;      // blocks of the rank kernel (1024 slots each)
+    int max_tiles;        // tile-table capacity: ceil(slots / bn) + n_expert
+    int64_t off_rank, off_hist, off_offsets, off_sorted, off_tile_e, off_tile_r0, off_ntiles;
+};
+
+// Limits of MUL_MAT_ID_BACK: experts per op (the rank kernel's LDS tables).
+constexpr int kIdMaxExperts = 512;
+constexpr int kIdRankBlock = 1024;  // slots per rank-kernel block (16 waves)
+
+bool plan_id_back(IdProblem &p, Launch *l);   // sets the tile config and table layout
+int64_t id_workspace_bytes(const IdProblem &p);
+hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s);
+
 // Per-kernel planning (host only, no HIP calls) and launching.
 bool plan_skinny(const Problem &p, Launch *l);
 bool plan_tiled(const Problem &p, Launch *l);

@@ -158,6 +158,64 @@ struct F32LoaderKT {
     }
 };
 
+// f32 b columns gathered from anywhere (the routed slots of one expert in
+// MUL_MAT_ID_BACK): column n of the tile starts at cols[n] (nullptr: no
+// column) and holds K contiguous floats; groups of 4 consecutive k written
+// transposed into the [k][column] LDS tile.  vec: every column start is
+// 16-byte aligned.
+template <int BW, int BK, int T>
+struct GatherLoaderKT {
+    static constexpr int kGroups = BK / 4 * BW;
+    static constexpr int kPer = (kGroups + T - 1) / T;
+    static_assert(BK % 4 == 0, "stage rows must be a multiple of 4");
+    const uint8_t *col[kPer];
+    int K, tid;
+    bool vec;
+    floatx4 r[kPer];
+
+    __device__ void init(const uint8_t *const *cols, int k_len, bool vec_ok, int t) {
+        K = k_len;
+        vec = vec_ok;
+        tid = t;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int g = tid + T * j;
+            col[j] = (kGroups % T == 0 || g < kGroups) ? cols[g % BW] : nullptr;
+        }
+    }
+    __device__ void load(int k0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int g = tid + T * j;
+            const int k = k0 + 4 * (g / BW);
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (col[j] != nullptr && k < K) {
+                const uint8_t *ptr = col[j] + (int64_t)k * 4;
+                if (vec && k + 3 < K) {
+                    v = *(const floatx4 *)ptr;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k + e < K) v[e] = ldf(ptr + 4 * e);
+                }
+            }
+            r[j] = v;
+        }
+    }
+    template <int LD>
+    __device__ void store(float (*lds)[LD]) const {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int g = tid + T * j;
+            if (kGroups % T == 0 || g < kGroups) {
+                const int n = g % BW, kq = g / BW;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lds[4 * kq + e][n] = r[j][e];
+            }
+        }
+    }
+};
+
 // q8_0 a: groups of 8 consecutive values of one 32-value block.  34-byte
 // blocks are only 2-byte aligned, so the codes come in as 16-bit loads.
 template <int BM, int BK, int T>
@@ -489,21 +547,115 @@ __host__ __device__ constexpr int lds_ld(int bw, int mf) {
 
 // ---------------------------------------------------------------- kernel
 
+// One workgroup's BM x BN tile: the K loop shared by the OUT_PROD kernel and
+// the grouped MUL_MAT_ID_BACK kernel.  WGM x WGN waves, each with FM x FN
+// MFMA blocks of MF x MF; BK rows of K per pipeline stage.
+template <int MF, int FM, int FN, int WGM, int WGN, int BK>
+struct TileCore {
+    typedef Mfma<MF> MM;
+    typedef typename MM::acc_t acc_t;
+    static constexpr int T = 64 * WGM * WGN;
+    static constexpr int WTM = MF * FM, WTN = MF * FN;
+    static constexpr int BM = WTM * WGM, BN = WTN * WGN;
+    static constexpr int LDA = lds_ld(BM, MF), LDB = lds_ld(BN, MF);
+    static constexpr int S = BK / MM::KS;  // MFMA steps per stage
+    static_assert(BK % MM::KS == 0 && S % 2 == 0, "stage must hold an even number of MFMA steps");
+
+    // acc = the tile's sum over k < K of a-rows x b-rows, from the loaders'
+    // stages.  Ends with a barrier (the LDS buffers may be reused).  A wave
+    // with mma == false (wave-uniform) still loads and synchronizes but skips
+    // its MFMAs: its rows of the tile are not needed, and the SIMD cycles go
+    // to the other workgroups on the CU.
+    template <class LA, class LB>
+    __device__ static void run(LA &la, LB &lb, int K, float (&As)[2][BK][LDA],
+                               float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN], bool mma = true) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave % WGM, wn = wave / WGM;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
+
+        const int ktiles = (K + BK - 1) / BK;
+        la.load(0);
+        lb.load(0);
+        la.store(As[0]);
+        lb.store(Bs[0]);
+        if (ktiles > 1) {
+            la.load(BK);
+            lb.load(BK);
+        }
+        __syncthreads();
+
+        const int kq = lane / MF, col = lane % MF;
+        const int a_col = wm * WTM + col, b_col = wn * WTN + col;
+
+        // MFMA steps [s0, s1) of a stage.  Operand fragments are double-buffered
+        // in registers: step st+1's LDS reads are issued before step st's MFMAs.
+        auto mfma_steps = [&](int cur, int s0, int s1) {
+            float af[2][FM], bf[2][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[0][i] = As[cur][MM::KS * s0 + kq][a_col + MF * i];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][MM::KS * s0 + kq][b_col + MF * j];
+#pragma unroll
+            for (int st = s0; st < s1; ++st) {
+                const int x = (st - s0) & 1;
+                if (st + 1 < s1) {
+                    const int kr = MM::KS * (st + 1) + kq;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
+            }
+        };
+
+        for (int t = 0; t < ktiles; ++t) {
+            const int cur = t & 1;
+            if (mma) mfma_steps(cur, 0, S / 2);
+            if (t + 1 < ktiles) {
+                // registers hold stage t+1: decode into the free buffer, then
+                // start stage t+2's loads
+                la.store(As[cur ^ 1]);
+                lb.store(Bs[cur ^ 1]);
+                if (t + 2 < ktiles) {
+                    la.load((t + 2) * BK);
+                    lb.load((t + 2) * BK);
+                }
+            }
+            if (mma) mfma_steps(cur, S / 2, S);
+            __syncthreads();
+        }
+    }
+
+    // Tile-relative dst position of accumulator (i, j, register r) of this
+    // lane: column (along i0) and row (along i1).
+    __device__ static int col_of(int i) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        return (wave % WGM) * WTM + lane % MF + MF * i;
+    }
+    __device__ static int row_of(int j, int r) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        return (wave / WGM) * WTN + MF * j + MM::row(r, lane);
+    }
+};
+
 template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int tiles_m,
                                                                int tiles_n) {
-    typedef Mfma<MF> MM;
-    constexpr int T = 64 * WGM * WGN;
-    constexpr int WTM = MF * FM, WTN = MF * FN;
-    constexpr int BM = WTM * WGM, BN = WTN * WGN;
-    constexpr int LDA = lds_ld(BM, MF), LDB = lds_ld(BN, MF);
-    constexpr int S = BK / MM::KS;  // MFMA steps per stage
-    static_assert(BK % MM::KS == 0 && S % 2 == 0, "stage must hold an even number of MFMA steps");
-    __shared__ __attribute__((aligned(16))) float As[2][BK][LDA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDB];
+    typedef TileCore<MF, FM, FN, WGM, WGN, BK> C;
+    constexpr int T = C::T, BM = C::BM, BN = C::BN;
+    __shared__ __attribute__((aligned(16))) float As[2][BK][C::LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK][C::LDB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WGM, wn = wave / WGM;
+    const int tid = threadIdx.x;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int per_slice = tiles_m * tiles_n;
     // split range outermost, so the tiles of one K range share the XCDs'
@@ -522,80 +674,85 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
 
-    typename MM::acc_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
-
-    const int ktiles = (K + BK - 1) / BK;
-    la.load(0);
-    lb.load(0);
-    la.store(As[0]);
-    lb.store(Bs[0]);
-    if (ktiles > 1) {
-        la.load(BK);
-        lb.load(BK);
-    }
-    __syncthreads();
-
-    const int kq = lane / MF, col = lane % MF;
-    const int a_col = wm * WTM + col, b_col = wn * WTN + col;
-
-    // MFMA steps [s0, s1) of a stage.  Operand fragments are double-buffered
-    // in registers: step st+1's LDS reads are issued before step st's MFMAs.
-    auto mfma_steps = [&](int cur, int s0, int s1) {
-        float af[2][FM], bf[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[0][i] = As[cur][MM::KS * s0 + kq][a_col + MF * i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][MM::KS * s0 + kq][b_col + MF * j];
-#pragma unroll
-        for (int st = s0; st < s1; ++st) {
-            const int x = (st - s0) & 1;
-            if (st + 1 < s1) {
-                const int kr = MM::KS * (st + 1) + kq;
-#pragma unroll
-                for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
-#pragma unroll
-                for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
-        }
-    };
-
-    for (int t = 0; t < ktiles; ++t) {
-        const int cur = t & 1;
-        mfma_steps(cur, 0, S / 2);
-        if (t + 1 < ktiles) {
-            // registers hold stage t+1: decode into the free buffer, then
-            // start stage t+2's loads
-            la.store(As[cur ^ 1]);
-            lb.store(Bs[cur ^ 1]);
-            if (t + 2 < ktiles) {
-                la.load((t + 2) * BK);
-                lb.load((t + 2) * BK);
-            }
-        }
-        mfma_steps(cur, S / 2, S);
-        __syncthreads();
-    }
+    typename C::acc_t acc[FM][FN];
+    C::run(la, lb, K, As, Bs, acc);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int i0 = m0 + a_col + MF * i;
+        const int i0 = m0 + C::col_of(i);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int r = 0; r < MM::NR; ++r) {
-                const int i1 = n0 + wn * WTN + MF * j + MM::row(r, lane);
+            for (int r = 0; r < C::MM::NR; ++r) {
+                const int i1 = n0 + C::row_of(j, r);
                 if (i0 < M && i1 < N)
                     *(float *)(s.dst + (int64_t)i1 * p.nb1 + (int64_t)i0 * 4) = acc[i][j][r];
+            }
+        }
+    }
+}
+
+// Grouped MUL_MAT_ID_BACK: workgroup (tile j of the routing table, m-tile)
+// multiplies expert tile_e[j] by the gradient columns of up to BN of its
+// routed slots (sorted[offsets[e] + tile_r0[j] + n]) and writes each slot's
+// dst row segment.  Workgroups past the table's n_tiles exit at once.
+template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK>
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, int tiles_m) {
+    typedef TileCore<MF, FM, FN, WGM, WGN, BK> C;
+    constexpr int T = C::T, BM = C::BM, BN = C::BN;
+    __shared__ __attribute__((aligned(16))) float As[2][BK][C::LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK][C::LDB];
+    __shared__ const uint8_t *gcol[BN];
+    __shared__ uint8_t *drow[BN];
+
+    const int tid = threadIdx.x;
+    // The grid is sized for the most tiles any routing can need; only the
+    // first tiles_m * n_tiles blocks have work.  The dispatcher deals blocks
+    // to the XCDs round-robin, so the working blocks cover every XCD; the
+    // remap over exactly those blocks keeps each XCD's tiles contiguous.
+    const int *ws = (const int *)p.ws;
+    const int real = tiles_m * ws[p.off_ntiles];
+    if ((int)blockIdx.x >= real) return;  // uniform: the whole workgroup exits
+    const int logical = xcd_remap(blockIdx.x, real);
+    const int j = logical / tiles_m, m0 = (logical % tiles_m) * BM;
+    const int e = ws[p.off_tile_e + j];
+    const int first = ws[p.off_offsets + e] + ws[p.off_tile_r0 + j];
+    const int end = ws[p.off_offsets + e + 1];
+    const int cnt = end - first < BN ? end - first : BN;
+    const int nu = (int)p.n_used;
+    for (int n = tid; n < BN; n += T) {
+        if (n < cnt) {
+            const int slot = ws[p.off_sorted + first + n];
+            const int i = slot % nu, t = slot / nu;
+            gcol[n] = p.g + (int64_t)i * p.nbg1 + (int64_t)t * p.nbg2;
+            drow[n] = p.dst + (int64_t)i * p.nbd1 + (int64_t)t * p.nbd2;
+        } else {
+            gcol[n] = nullptr;
+            drow[n] = nullptr;
+        }
+    }
+    __syncthreads();
+    const int K = (int)p.K, M = (int)p.M;
+
+    typename ALoaderFor<AT, BM, BK, T>::type la;
+    GatherLoaderKT<BN, BK, T> lb;
+    la.init(p.as + (int64_t)e * p.nb02, p.nb01, M, K, m0, p.vec_a, tid);
+    lb.init(gcol, K, p.vec_g, tid);
+
+    // waves whose slot rows are all past the expert's last slot skip their MFMAs
+    typename C::acc_t acc[FM][FN];
+    const int wave_row0 = (int)(threadIdx.x >> 6) / WGM * C::WTN;  // the wave's first slot row
+    C::run(la, lb, K, As, Bs, acc, wave_row0 < cnt);
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int i0 = m0 + C::col_of(i);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+#pragma unroll
+            for (int r = 0; r < C::MM::NR; ++r) {
+                const int n = C::row_of(jj, r);
+                if (i0 < M && n < cnt) *(float *)(drow[n] + (int64_t)i0 * 4) = acc[i][jj][r];
             }
         }
     }
@@ -624,6 +781,10 @@ struct TileCfg {
 // 7: 128 x 128, 4 waves of 64 x 64 (32x32x2), 32-row stages
 // 8: as 1 with 32-row stages
 // 9: as 3 with 32-row stages
+// 10: as 2 with 32-row stages
+// 11: as 4 with 32-row stages
+// 12: 128 x 80, 4 waves of 32 x 80 (16x16x4) -- 80-slot tiles (routed experts)
+// 13: 64 x 80,  4 waves of 16 x 80 (16x16x4)
 constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 16, 12.4f},
     {16, 5, 2, 2, 4, 16, 11.5f},
@@ -635,6 +796,10 @@ constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 32, 12.0f},
     {16, 5, 2, 2, 4, 32, 12.2f},
     {16, 17, 1, 1, 8, 32, 12.1f},
+    {16, 5, 2, 2, 2, 32, 10.3f},
+    {32, 1, 1, 2, 2, 32, 10.5f},
+    {16, 2, 5, 4, 1, 16, 10.4f},
+    {16, 1, 5, 4, 1, 16, 10.0f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -656,6 +821,10 @@ const void *tiled_fn(int variant) {
     case 7: return cfg_fn<AT, 7, BT>();
     case 8: return cfg_fn<AT, 8, BT>();
     case 9: return cfg_fn<AT, 9, BT>();
+    case 10: return cfg_fn<AT, 10, BT>();
+    case 11: return cfg_fn<AT, 11, BT>();
+    case 12: return cfg_fn<AT, 12, BT>();
+    case 13: return cfg_fn<AT, 13, BT>();
     default: return cfg_fn<AT, 0, BT>();
     }
 }
@@ -665,14 +834,42 @@ const void *tiled_fn(int variant, bool bt) {
     return bt ? tiled_fn<AT, true>(variant) : tiled_fn<AT, false>(variant);
 }
 
-// The kernel for a type, configuration and b layout; defined by the
-// instantiation files (one per group of a types).  nullptr: type not built.
-const void *tiled_kernel_f32(int a_type, int variant, bool bt);
-const void *tiled_kernel_half(int a_type, int variant, bool bt);
-const void *tiled_kernel_q8(int a_type, int variant, bool bt);
-const void *tiled_kernel_q45(int a_type, int variant, bool bt);
-const void *tiled_kernel_k4(int a_type, int variant, bool bt);
-const void *tiled_kernel_k(int a_type, int variant, bool bt);
+// Tile configurations the grouped MUL_MAT_ID_BACK kernel is built for
+// (indices into kCfgs): 64-, 80- and 128-slot tiles, 16- and 32-row stages.
+constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13};
+constexpr int kNumIdCfgs = sizeof(kIdCfgs) / sizeof(kIdCfgs[0]);
+
+template <int AT, int C>
+const void *id_cfg_fn() {
+    constexpr TileCfg c = kCfgs[C];
+    return (const void *)&tiled_id_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk>;
+}
+
+template <int AT>
+const void *id_fn(int cfg) {
+    switch (cfg) {
+    case 2: return id_cfg_fn<AT, 2>();
+    case 4: return id_cfg_fn<AT, 4>();
+    case 1: return id_cfg_fn<AT, 1>();
+    case 0: return id_cfg_fn<AT, 0>();
+    case 8: return id_cfg_fn<AT, 8>();
+    case 10: return id_cfg_fn<AT, 10>();
+    case 11: return id_cfg_fn<AT, 11>();
+    case 12: return id_cfg_fn<AT, 12>();
+    case 13: return id_cfg_fn<AT, 13>();
+    default: return nullptr;
+    }
+}
+
+// The kernel for a type, configuration and b layout (and, with id = true,
+// the grouped MUL_MAT_ID_BACK kernel for a type and configuration); defined
+// by the instantiation files (one per group of a types).  nullptr: not built.
+const void *tiled_kernel_f32(int a_type, int variant, bool bt, bool id = false);
+const void *tiled_kernel_half(int a_type, int variant, bool bt, bool id = false);
+const void *tiled_kernel_q8(int a_type, int variant, bool bt, bool id = false);
+const void *tiled_kernel_q45(int a_type, int variant, bool bt, bool id = false);
+const void *tiled_kernel_k4(int a_type, int variant, bool bt, bool id = false);
+const void *tiled_kernel_k(int a_type, int variant, bool bt, bool id = false);
 
 }  // namespace tiled
 }  // namespace outprod

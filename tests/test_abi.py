@@ -158,7 +158,7 @@ def test_forced_kernels():
         assert p["kernel_name"] == "skinny" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 11))] == "E_KERNEL"
     # every tiled configuration can be forced; an unknown one is refused
-    for cfg in range(10):
+    for cfg in range(14):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, 40))] == "E_KERNEL"
@@ -271,3 +271,65 @@ def test_every_a_type_plans(a_type):
     # the skinny kernel is f32 only
     if a_type != synth.F32:
         assert B.STATUS[plan(a_type, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
+
+
+# ---------------------------------------------------------------- MUL_MAT_ID_BACK
+
+G_ = 0x50000000000
+I_ = 0x60000000000
+
+
+def id_plan(inst, a=A, g=G_, ids=I_, d=D, ne=None, nb=None, kernel=0):
+    return B.id_back_plan_status(a, inst.a_type, g, ids, d, ne or inst.ne, nb or inst.nb, kernel)
+
+
+def test_id_back_plans_and_refusals():
+    inst = synth.make_moe_instance("abi", synth.Q4_K, 512, 96, 8, 2, 40, 1)
+    p = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb)
+    assert p["kernel_name"] == "tiled" and p["slices"] == 80 and p["flops"] == 2 * 512 * 96 * 80
+    assert p["workspace_bytes"] > 0 and p["grid"] >= 1
+    for cfg in (0, 1, 2, 4, 8, 10, 11, 12, 13):
+        q = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb,
+                                    B.kernel_code(B.KERNEL_TILED, cfg))
+        assert q["variant"] == cfg
+    assert B.STATUS[id_plan(inst, kernel=B.kernel_code(B.KERNEL_TILED, 3))] == "E_KERNEL"
+    assert B.STATUS[id_plan(inst, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
+    assert B.STATUS[id_plan(inst, kernel=B.kernel_code(B.KERNEL_TILED, None, 2))] == "E_KERNEL"
+    ne = list(inst.ne)
+    ne[4] = 95
+    assert B.STATUS[id_plan(inst, ne=ne)] == "E_K"
+    ne = list(inst.ne)
+    ne[13] = 3
+    assert B.STATUS[id_plan(inst, ne=ne)] == "E_DST_SHAPE"
+    ne = list(inst.ne)
+    ne[8] = 3
+    assert B.STATUS[id_plan(inst, ne=ne)] == "E_SHAPE"
+    ne = list(inst.ne)
+    ne[0] = ne[12] = 384
+    assert B.STATUS[id_plan(inst, ne=ne)] == "E_QK"
+    nb = list(inst.nb)
+    nb[4] = 8           # g must be K-contiguous
+    assert B.STATUS[id_plan(inst, nb=nb)] == "E_LAYOUT"
+    nb = list(inst.nb)
+    nb[13] = 4 * 500    # dst rows overlap
+    assert B.STATUS[id_plan(inst, nb=nb)] == "E_LAYOUT"
+    assert B.STATUS[id_plan(inst, ids=0)] == "E_NULL"
+    assert B.STATUS[id_plan(inst, ids=I_ + 2)] == "E_LAYOUT"
+    assert B.STATUS[id_plan(inst, d=G_ + 64)] == "E_ALIAS"
+    assert B.STATUS[id_plan(inst, d=I_)] == "E_ALIAS"
+    big = synth.moe_ne_nb(synth.Q4_K, 256, 8, 513, 2, 4)
+    assert B.STATUS[B.id_back_plan_status(A, synth.Q4_K, G_, I_, D, *big)] == "E_RANGE"
+    # nothing to do: no tokens; K == 0: zeros
+    ne0, nb0 = synth.moe_ne_nb(synth.F32, 16, 8, 4, 2, 0)
+    assert B.out_prod_id_back_plan(A, synth.F32, G_, I_, D, ne0, nb0)["kernel_name"] == "none"
+    ne0, nb0 = synth.moe_ne_nb(synth.F32, 16, 0, 4, 2, 3)
+    assert B.out_prod_id_back_plan(A, synth.F32, G_, I_, D, ne0, nb0)["kernel_name"] == "zero"
+    assert B.out_prod_id_back_plan(0, synth.F32, 0, 0, D, ne0, nb0)["kernel_name"] == "zero"
+
+
+@pytest.mark.parametrize("a_type", ALL_TYPES)
+def test_id_back_every_type_plans(a_type):
+    qk = synth.BLOCK_VALUES[a_type]
+    inst_ne, inst_nb = synth.moe_ne_nb(a_type, 256 if qk > 1 else 100, 64, 4, 2, 8)
+    p = B.out_prod_id_back_plan(A, a_type, G_, I_, D, inst_ne, inst_nb)
+    assert p["kernel_name"] == "tiled"
