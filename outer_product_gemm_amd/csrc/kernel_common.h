@@ -23,18 +23,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// IEEE binary16 bits -> float, exactly, by bit manipulation (normal numbers
-// are rebiased, subnormals are f * 2^-24, Inf/NaN keep their class).
+// IEEE binary16 bits (the low 16 of h) -> float.  Every binary16 value,
+// subnormals included, is exactly a binary32 value, and the hardware
+// conversion (v_cvt_f32_f16) is exact: half denormals are kept in the default
+// float mode.  Inf/NaN keep their class.
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    const uint32_t sign = (h & 0x8000u) << 16;
-    const uint32_t e = (h >> 10) & 0x1Fu;
-    const uint32_t f = h & 0x3FFu;
-    if (e == 0) {
-        const float v = (float)f * 0x1p-24f;  // f < 2^10: exact
-        return __uint_as_float(__float_as_uint(v) | sign);
-    }
-    const uint32_t ee = e == 31 ? 0xFFu : e + 112u;
-    return __uint_as_float(sign | (ee << 23) | (f << 13));
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // Grouped-head broadcast: dst slice z = i2 + ne12*i3 reads a slice

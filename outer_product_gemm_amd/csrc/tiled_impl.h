@@ -67,6 +67,9 @@ struct F32Loader {
         vec = vec_ok;
         tid = t;
     }
+    // FULL: the whole tile is in range and 16-byte aligned (uniform,
+    // checked by the caller): unconditional vector loads.
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -74,7 +77,10 @@ struct F32Loader {
             const int row = g / (BW / 4), c = w0 + 4 * (g % (BW / 4));
             const int k = k0 + row;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if ((kGroups % T == 0 || g < kGroups) && k < K) {
+            if (FULL) {
+                if (kGroups % T == 0 || g < kGroups)
+                    v = *(const floatx4 *)(base + (int64_t)k * ld + (int64_t)c * 4);
+            } else if ((kGroups % T == 0 || g < kGroups) && k < K) {
                 const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)c * 4;
                 if (vec && c + 3 < W) {
                     v = *(const floatx4 *)ptr;
@@ -124,6 +130,7 @@ struct F32LoaderKT {
         vec = vec_ok;
         tid = t;
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -131,7 +138,10 @@ struct F32LoaderKT {
             const int n = g % BW, kq = g / BW;
             const int c = w0 + n, k = k0 + 4 * kq;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if ((kGroups % T == 0 || g < kGroups) && c < W) {
+            if (FULL) {
+                if (kGroups % T == 0 || g < kGroups)
+                    v = *(const floatx4 *)(base + (int64_t)c * ld + (int64_t)k * 4);
+            } else if ((kGroups % T == 0 || g < kGroups) && c < W) {
                 const uint8_t *ptr = base + (int64_t)c * ld + (int64_t)k * 4;
                 if (vec && k + 3 < K) {
                     v = *(const floatx4 *)ptr;
@@ -183,13 +193,16 @@ struct GatherLoaderKT {
             col[j] = (kGroups % T == 0 || g < kGroups) ? cols[g % BW] : nullptr;
         }
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
             const int k = k0 + 4 * (g / BW);
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if (col[j] != nullptr && k < K) {
+            if (FULL) {
+                if (kGroups % T == 0 || g < kGroups) v = *(const floatx4 *)(col[j] + (int64_t)k * 4);
+            } else if (col[j] != nullptr && k < K) {
                 const uint8_t *ptr = col[j] + (int64_t)k * 4;
                 if (vec && k + 3 < K) {
                     v = *(const floatx4 *)ptr;
@@ -238,6 +251,7 @@ struct Q8Loader {
         m0 = col0;
         tid = t;
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -246,7 +260,7 @@ struct Q8Loader {
             const int k = k0 + row;
             d[j] = 0;
             q[j][0] = q[j][1] = q[j][2] = q[j][3] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 5) * 34;
                 const uint16_t *qs = (const uint16_t *)(blk + 2 + (m & 31));
                 d[j] = *(const uint16_t *)blk;
@@ -296,6 +310,7 @@ struct Q4KLoader {
         m0 = col0;
         tid = t;
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -303,7 +318,7 @@ struct Q4KLoader {
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             dd[j] = s0[j] = s1[j] = s2[j] = q0[j] = q1[j] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 8) * 144;
                 const int w = m & 255, sub = w >> 5, pos = w & 31;
                 const uint32_t *hdr = (const uint32_t *)blk;
@@ -326,30 +341,29 @@ struct Q4KLoader {
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             const int sub = ((m0 + c) & 255) >> 5;
             // 6-bit scale and min of sub-block `sub` from the 12 packed bytes
-            // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2): for sub < 4 the low 6
-            // bits of bytes sub and 4+sub; otherwise the nibbles of byte
-            // 8+(sub-4) below the top two bits of bytes sub-4 and sub.
-            uint32_t sc, mn;
-            if (sub < 4) {
-                sc = (s0[j] >> (8 * sub)) & 0x3Fu;
-                mn = (s1[j] >> (8 * sub)) & 0x3Fu;
-            } else {
-                const int sh = 8 * (sub - 4);
-                const uint32_t lo = (s2[j] >> sh) & 0xFFu;
-                sc = (lo & 0x0Fu) | ((((s0[j] >> sh) >> 6) & 0x3u) << 4);
-                mn = (lo >> 4) | ((((s1[j] >> sh) >> 6) & 0x3u) << 4);
-            }
+            // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2), without branches: for
+            // sub < 4 the low 6 bits of bytes sub and 4+sub; otherwise the
+            // nibbles of byte 8+(sub-4) below the top two bits of bytes sub-4
+            // and sub.
+            const int sh = 8 * (sub & 3);
+            const uint32_t b0 = (s0[j] >> sh) & 0xFFu, b1 = (s1[j] >> sh) & 0xFFu;
+            const uint32_t b2 = (s2[j] >> sh) & 0xFFu;
+            const bool hi = sub >= 4;
+            const uint32_t sc = hi ? (b2 & 0x0Fu) | ((b0 >> 6) << 4) : (b0 & 0x3Fu);
+            const uint32_t mn = hi ? (b2 >> 4) | ((b1 >> 6) << 4) : (b1 & 0x3Fu);
             const float d = half_bits_to_float(dd[j] & 0xFFFFu);
             const float dmin = half_bits_to_float(dd[j] >> 16);
             const float ds = d * (float)sc;    // exact: <= 17 significant bits
             const float dm = dmin * (float)mn; // exact
+            // this sub-block's nibble of each of the 8 code bytes, as bytes
             const int shift = (sub & 1) ? 4 : 0;
+            const uint32_t n0 = (q0[j] >> shift) & 0x0F0F0F0Fu, n1 = (q1[j] >> shift) & 0x0F0F0F0Fu;
             float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // value = d*sc*q - dmin*m: the product is exact, one rounding
-                v[e] = ds * (float)((q0[j] >> (8 * e + shift)) & 0xFu) - dm;
-                v[4 + e] = ds * (float)((q1[j] >> (8 * e + shift)) & 0xFu) - dm;
+                v[e] = ds * (float)((n0 >> (8 * e)) & 0xFFu) - dm;
+                v[4 + e] = ds * (float)((n1 >> (8 * e)) & 0xFFu) - dm;
             }
             *(floatx4 *)&lds[row][c] = floatx4{v[0], v[1], v[2], v[3]};
             *(floatx4 *)&lds[row][c + 4] = floatx4{v[4], v[5], v[6], v[7]};
@@ -382,6 +396,7 @@ struct HalfLoader {
         vec = vec_ok;
         tid = t;
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -389,9 +404,9 @@ struct HalfLoader {
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             r[j][0] = r[j][1] = r[j][2] = r[j][3] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)m * 2;
-                if (vec && m + 7 < M) {
+                if (FULL || (vec && m + 7 < M)) {
                     const uint4 q = *(const uint4 *)ptr;
                     r[j][0] = q.x;
                     r[j][1] = q.y;
@@ -445,6 +460,7 @@ struct BlockLoader {
         m0 = col0;
         tid = t;
     }
+    template <bool FULL>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -453,7 +469,7 @@ struct BlockLoader {
             const int k = k0 + row;
 #pragma unroll
             for (int x = 0; x < F::NW; ++x) r[j][x] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && k < K && m < M) {
+            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m / F::QK) * F::BYTES;
                 F::fetch(blk, m % F::QK, r[j]);
             }
@@ -566,7 +582,7 @@ struct TileCore {
     // with mma == false (wave-uniform) still loads and synchronizes but skips
     // its MFMAs: its rows of the tile are not needed, and the SIMD cycles go
     // to the other workgroups on the CU.
-    template <class LA, class LB>
+    template <bool FULL, class LA, class LB>
     __device__ static void run(LA &la, LB &lb, int K, float (&As)[2][BK][LDA],
                                float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN], bool mma = true) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -579,13 +595,13 @@ struct TileCore {
                 for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
 
         const int ktiles = (K + BK - 1) / BK;
-        la.load(0);
-        lb.load(0);
+        la.template load<FULL>(0);
+        lb.template load<FULL>(0);
         la.store(As[0]);
         lb.store(Bs[0]);
         if (ktiles > 1) {
-            la.load(BK);
-            lb.load(BK);
+            la.template load<FULL>(BK);
+            lb.template load<FULL>(BK);
         }
         __syncthreads();
 
@@ -626,8 +642,8 @@ struct TileCore {
                 la.store(As[cur ^ 1]);
                 lb.store(Bs[cur ^ 1]);
                 if (t + 2 < ktiles) {
-                    la.load((t + 2) * BK);
-                    lb.load((t + 2) * BK);
+                    la.template load<FULL>((t + 2) * BK);
+                    lb.template load<FULL>((t + 2) * BK);
                 }
             }
             if (mma) mfma_steps(cur, S / 2, S);
@@ -674,8 +690,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
 
+    // whole tile in range, whole stages, 16-byte aligned operands: the loads
+    // need no per-lane checks
+    const bool a_vec_ok = (AT != OUTPROD_TYPE_F32 && AT != OUTPROD_TYPE_F16 && AT != OUTPROD_TYPE_BF16) ||
+                          p.vec_a;
+    const bool full = m0 + BM <= M && n0 + BN <= N && K % BK == 0 && a_vec_ok && p.vec_b;
     typename C::acc_t acc[FM][FN];
-    C::run(la, lb, K, As, Bs, acc);
+    if (full)
+        C::template run<true>(la, lb, K, As, Bs, acc);
+    else
+        C::template run<false>(la, lb, K, As, Bs, acc);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -742,7 +766,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, i
     // waves whose slot rows are all past the expert's last slot skip their MFMAs
     typename C::acc_t acc[FM][FN];
     const int wave_row0 = (int)(threadIdx.x >> 6) / WGM * C::WTN;  // the wave's first slot row
-    C::run(la, lb, K, As, Bs, acc, wave_row0 < cnt);
+    const bool a_vec_ok = (AT != OUTPROD_TYPE_F32 && AT != OUTPROD_TYPE_F16 && AT != OUTPROD_TYPE_BF16) ||
+                          p.vec_a;
+    const bool full = m0 + BM <= M && cnt == BN && K % BK == 0 && a_vec_ok && p.vec_g;
+    if (full)
+        C::template run<true>(la, lb, K, As, Bs, acc, wave_row0 < cnt);
+    else
+        C::template run<false>(la, lb, K, As, Bs, acc, wave_row0 < cnt);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
