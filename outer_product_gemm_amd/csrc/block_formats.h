@@ -38,6 +38,11 @@ __device__ __forceinline__ uint32_t ld_u32_a2(const uint8_t *p) {
 __device__ __forceinline__ uint32_t byte_of(uint32_t lo, uint32_t hi, int e) {
     return ((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu;
 }
+// byte e of a dword as float (one v_cvt_f32_ubyte)
+__device__ __forceinline__ float ubyte(uint32_t w, int e) { return (float)((w >> (8 * e)) & 0xFFu); }
+// bits 0-3 of x moved to bit 0 of bytes 0-3 (the four partial products do
+// not overlap, so the multiply has no carries into the kept bits)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0x00204081u) & 0x01010101u; }
 
 // q4_0: fp16 d; 16 code bytes -- byte j holds value j (low nibble) and value
 // j+16 (high nibble); value = d*(q - 8).
@@ -49,11 +54,15 @@ struct FmtQ4_0 {
         r[2] = ld_u32_a2(blk + 6 + (w & 15));
     }
     __device__ static void decode(const uint32_t (&r)[NW], int w, float (&v)[8]) {
-        const float d = half_bits_to_float(r[0]);
+        const float d = half_bits_to_float(r[0]), off = -8.f * d;  // exact
         const int sh = w >= 16 ? 4 : 0;
+        const uint32_t n0 = (r[1] >> sh) & 0x0F0F0F0Fu, n1 = (r[2] >> sh) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = d * (float)((int)((byte_of(r[1], r[2], e) >> sh) & 0xFu) - 8);
+        for (int e = 0; e < 4; ++e) {
+            // d*q - 8d = d*(q - 8): exact (<= 15 significant bits)
+            v[e] = __builtin_fmaf(d, ubyte(n0, e), off);
+            v[4 + e] = __builtin_fmaf(d, ubyte(n1, e), off);
+        }
     }
 };
 
@@ -68,8 +77,12 @@ struct FmtQ4_1 {
     __device__ static void decode(const uint32_t (&r)[NW], int w, float (&v)[8]) {
         const float d = half_bits_to_float(r[0] & 0xFFFFu), m = half_bits_to_float(r[0] >> 16);
         const int sh = w >= 16 ? 4 : 0;
+        const uint32_t n0 = (r[1] >> sh) & 0x0F0F0F0Fu, n1 = (r[2] >> sh) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = d * (float)((byte_of(r[1], r[2], e) >> sh) & 0xFu) + m;
+        for (int e = 0; e < 4; ++e) {  // d*q exact, one rounding with + m
+            v[e] = __builtin_fmaf(d, ubyte(n0, e), m);
+            v[4 + e] = __builtin_fmaf(d, ubyte(n1, e), m);
+        }
     }
 };
 
@@ -84,13 +97,15 @@ struct FmtQ5_0 {
         r[3] = ld_u32_a2(blk + 10 + (w & 15));
     }
     __device__ static void decode(const uint32_t (&r)[NW], int w, float (&v)[8]) {
-        const float d = half_bits_to_float(r[0]);
+        const float d = half_bits_to_float(r[0]), off = -16.f * d;  // exact
         const int sh = w >= 16 ? 4 : 0;
         const uint32_t hb = (r[1] >> (8 * ((w >> 3) & 1))) & 0xFFu;
+        const uint32_t n0 = ((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4);
+        const uint32_t n1 = ((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t q = ((byte_of(r[2], r[3], e) >> sh) & 0xFu) | (((hb >> e) & 1u) << 4);
-            v[e] = d * (float)((int)q - 16);
+        for (int e = 0; e < 4; ++e) {  // d*(q - 16): exact
+            v[e] = __builtin_fmaf(d, ubyte(n0, e), off);
+            v[4 + e] = __builtin_fmaf(d, ubyte(n1, e), off);
         }
     }
 };
@@ -108,10 +123,12 @@ struct FmtQ5_1 {
         const float d = half_bits_to_float(r[0] & 0xFFFFu), m = half_bits_to_float(r[0] >> 16);
         const int sh = w >= 16 ? 4 : 0;
         const uint32_t hb = (r[1] >> w) & 0xFFu;
+        const uint32_t n0 = ((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4);
+        const uint32_t n1 = ((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t q = ((byte_of(r[2], r[3], e) >> sh) & 0xFu) | (((hb >> e) & 1u) << 4);
-            v[e] = d * (float)q + m;
+        for (int e = 0; e < 4; ++e) {  // d*q exact, one rounding with + m
+            v[e] = __builtin_fmaf(d, ubyte(n0, e), m);
+            v[4 + e] = __builtin_fmaf(d, ubyte(n1, e), m);
         }
     }
 };
@@ -133,8 +150,12 @@ struct FmtQ2_K {
         const uint32_t sm = (r[1] >> (8 * ((w >> 4) & 3))) & 0xFFu;
         const float ds = d * (float)(sm & 0xFu), dm = dmin * (float)(sm >> 4);
         const int sh = 2 * ((w >> 5) & 3);
+        const uint32_t n0 = (r[2] >> sh) & 0x03030303u, n1 = (r[3] >> sh) & 0x03030303u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = ds * (float)((byte_of(r[2], r[3], e) >> sh) & 3u) - dm;
+        for (int e = 0; e < 4; ++e) {  // ds*q exact, one rounding with - dm
+            v[e] = __builtin_fmaf(ds, ubyte(n0, e), -dm);
+            v[4 + e] = __builtin_fmaf(ds, ubyte(n1, e), -dm);
+        }
     }
 };
 
@@ -163,11 +184,14 @@ struct FmtQ3_K {
         const uint32_t hi2 = (hib >> (2 * (i >> 2))) & 3u;
         const float dl = half_bits_to_float(r[0]) * (float)((int)(lo4 | (hi2 << 4)) - 32);
         const int hs = 4 * h + j;
+        // u = low | keep << 2 in each byte; q = u - 4 (keep set: q = low)
+        const uint32_t u0 = ((r[3] >> (2 * j)) & 0x03030303u) | (((r[1] >> hs) & 0x01010101u) << 2);
+        const uint32_t u1 = ((r[4] >> (2 * j)) & 0x03030303u) | (((r[2] >> hs) & 0x01010101u) << 2);
+        const float off = -4.f * dl;  // exact
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int low = (int)((byte_of(r[3], r[4], e) >> (2 * j)) & 3u);
-            const int keep = (int)((byte_of(r[1], r[2], e) >> hs) & 1u);
-            v[e] = dl * (float)(keep ? low : low - 4);
+        for (int e = 0; e < 4; ++e) {  // dl*(u - 4): exact
+            v[e] = __builtin_fmaf(dl, ubyte(u0, e), off);
+            v[4 + e] = __builtin_fmaf(dl, ubyte(u1, e), off);
         }
     }
 };
@@ -212,11 +236,12 @@ struct FmtQ5_K {
         const float ds = half_bits_to_float(r[0] & 0xFFFFu) * (float)sc;
         const float dm = half_bits_to_float(r[0] >> 16) * (float)mn;
         const int hs = 2 * g + s;
+        const uint32_t n0 = ((r[6] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[4] >> hs) & 0x01010101u) << 4);
+        const uint32_t n1 = ((r[7] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[5] >> hs) & 0x01010101u) << 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t q = ((byte_of(r[6], r[7], e) >> (4 * s)) & 0xFu) |
-                               (((byte_of(r[4], r[5], e) >> hs) & 1u) << 4);
-            v[e] = ds * (float)q - dm;
+        for (int e = 0; e < 4; ++e) {  // ds*q exact, one rounding with - dm
+            v[e] = __builtin_fmaf(ds, ubyte(n0, e), -dm);
+            v[4 + e] = __builtin_fmaf(ds, ubyte(n1, e), -dm);
         }
     }
 };
@@ -242,11 +267,13 @@ struct FmtQ6_K {
         const int sc = (int)(int8_t)((r[5] >> (8 * ((w >> 4) & 1))) & 0xFFu);
         const float ds = half_bits_to_float(r[0]) * (float)sc;  // exact: <= 19 bits
         const int ns = 4 * (c >> 1);
+        const uint32_t u0 = ((r[1] >> ns) & 0x0F0F0F0Fu) | (((r[3] >> (2 * c)) & 0x03030303u) << 4);
+        const uint32_t u1 = ((r[2] >> ns) & 0x0F0F0F0Fu) | (((r[4] >> (2 * c)) & 0x03030303u) << 4);
+        const float off = -32.f * ds;  // exact
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int q = (int)(((byte_of(r[1], r[2], e) >> ns) & 0xFu) |
-                                (((byte_of(r[3], r[4], e) >> (2 * c)) & 3u) << 4));
-            v[e] = ds * (float)(q - 32);
+        for (int e = 0; e < 4; ++e) {  // ds*(u - 32) rounded once, as d*scale*q
+            v[e] = __builtin_fmaf(ds, ubyte(u0, e), off);
+            v[4 + e] = __builtin_fmaf(ds, ubyte(u1, e), off);
         }
     }
 };

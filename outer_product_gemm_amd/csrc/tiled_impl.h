@@ -280,7 +280,8 @@ struct Q8Loader {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // value = d * q, exact in fp32 (11 + 7 significant bits)
+                // value = d * q, exact in fp32 (11 + 7 significant bits); the
+                // int8 -> float conversions are single sub-dword instructions
                 v[2 * e] = dd * (float)(int8_t)(q[j][e] & 0xFFu);
                 v[2 * e + 1] = dd * (float)(int8_t)(q[j][e] >> 8);
             }

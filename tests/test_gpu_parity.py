@@ -638,3 +638,35 @@ def test_every_type_dequant_bit_exact_one_hot(a_type):
         B.out_prod(a_d.data_ptr(), a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb, stream)
         got = out[: rows.size].cpu().numpy()
         assert np.array_equal(got, expect[rows]), (synth.TYPE_NAMES[a_type], start)
+
+
+@pytest.mark.parametrize("a_type", [synth.Q8_0, synth.Q4_K, synth.Q2_K, synth.Q6_K, synth.Q4_1, synth.F16])
+def test_subnormal_half_scales_bit_exact(a_type):
+    """fp16 scales (and f16 weights) that are subnormal, zero or negative decode
+    exactly: one-hot b reads the kernel's decoded values back, compared bit for
+    bit (as values) with the oracle's decode.  Pins the half -> float
+    conversion, subnormals included."""
+    M, K, N = 512, 64, 64
+    rng = synth.rng_for(seed_of("subn", a_type))
+    if a_type == synth.F16:
+        bits = rng.integers(0, 0x7C00, size=(K, M)).astype(np.uint16)      # finite, incl. subnormal
+        bits[:, ::3] = rng.integers(0, 0x0400, size=bits[:, ::3].shape)     # a third subnormal
+        bits |= (rng.integers(0, 2, size=bits.shape) << 15).astype(np.uint16)
+        a = bits
+    else:
+        a = synth.quant_rows(rng, a_type, K, M) if a_type in (synth.Q8_0, synth.Q4_K) else \
+            synth.block_rows(rng, a_type, K, M)
+        qk, bb = synth.BLOCK_VALUES[a_type], synth.BLOCK_BYTES[a_type]
+        blocks = a.reshape(K, M // qk, bb)
+        for off, _ in synth.HALF_FIELDS[a_type]:
+            h = rng.integers(0, 0x0400, size=blocks.shape[:2]).astype(np.uint16)   # subnormal or 0
+            h |= (rng.integers(0, 2, size=h.shape) << 15).astype(np.uint16)
+            blocks[:, :, off:off + 2] = h.reshape(K, -1, 1).view(np.uint8).reshape(K, -1, 2)
+        a = blocks.reshape(K, -1)
+    raw = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+    rowb = raw.size // K
+    expect = oracle.dequant_rows(raw, a_type, M, K, rowb)
+    ne, nb = synth.make_ne_nb(a_type, (M, K, 1, 1), (N, K, 1, 1))
+    b = np.eye(K, N, dtype=np.float32)        # column i1 picks row k = i1 of a
+    gpu = G.run(raw, a_type, b, ne, nb)
+    assert np.array_equal(gpu[0, 0], expect[:N])
