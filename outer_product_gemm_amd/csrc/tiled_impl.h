@@ -579,13 +579,13 @@ struct TileCore {
     static_assert(BK % MM::KS == 0 && S % 2 == 0, "stage must hold an even number of MFMA steps");
 
     // acc = the tile's sum over k < K of a-rows x b-rows, from the loaders'
-    // stages.  Ends with a barrier (the LDS buffers may be reused).  A wave
-    // with mma == false (wave-uniform) still loads and synchronizes but skips
-    // its MFMAs: its rows of the tile are not needed, and the SIMD cycles go
-    // to the other workgroups on the CU.
-    template <bool FULL, class LA, class LB>
+    // stages.  Ends with a barrier (the LDS buffers may be reused).  With
+    // PART, a wave runs only its first fn_act (wave-uniform) MFMA blocks along
+    // the tile's rows: the rows past them are not needed (a grouped tile
+    // holding fewer slots than its height), so those MFMAs are skipped.
+    template <bool FULL, bool PART = false, class LA, class LB>
     __device__ static void run(LA &la, LB &lb, int K, float (&As)[2][BK][LDA],
-                               float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN], bool mma = true) {
+                               float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN], int fn_act = FN) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave % WGM, wn = wave / WGM;
 #pragma unroll
@@ -630,9 +630,11 @@ struct TileCore {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
+                    for (int j = 0; j < FN; ++j)
+                        if (!PART || j < fn_act) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
             }
         };
+        const bool mma = !PART || fn_act > 0;
 
         for (int t = 0; t < ktiles; ++t) {
             const int cur = t & 1;
@@ -766,14 +768,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, i
 
     // waves whose slot rows are all past the expert's last slot skip their MFMAs
     typename C::acc_t acc[FM][FN];
+    // MFMA blocks of MF slot rows this wave needs: those holding a slot
     const int wave_row0 = (int)(threadIdx.x >> 6) / WGM * C::WTN;  // the wave's first slot row
+    const int need = (cnt - wave_row0 + MF - 1) / MF;
+    const int fn_act = need < 0 ? 0 : need > FN ? FN : need;
     const bool a_vec_ok = (AT != OUTPROD_TYPE_F32 && AT != OUTPROD_TYPE_F16 && AT != OUTPROD_TYPE_BF16) ||
                           p.vec_a;
     const bool full = m0 + BM <= M && cnt == BN && K % BK == 0 && a_vec_ok && p.vec_g;
     if (full)
-        C::template run<true>(la, lb, K, As, Bs, acc, wave_row0 < cnt);
+        C::template run<true>(la, lb, K, As, Bs, acc);
     else
-        C::template run<false>(la, lb, K, As, Bs, acc, wave_row0 < cnt);
+        C::template run<false, true>(la, lb, K, As, Bs, acc, fn_act);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
