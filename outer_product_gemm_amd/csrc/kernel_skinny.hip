@@ -77,6 +77,65 @@ __device__ __forceinline__ void load_a_group(const uint8_t *row, int i0, int M, 
     }
 }
 
+// W_ consecutive floats at ptr (16-byte aligned for W_ = 4, 8-byte for 2).
+template <int W_>
+__device__ __forceinline__ void ld_vec(const uint8_t *ptr, float *out) {
+    if constexpr (W_ == 1) {
+        out[0] = *(const float *)ptr;
+    } else {
+        const typename VecF<W_>::type v = *(const typename VecF<W_>::type *)ptr;
+#pragma unroll
+        for (int c = 0; c < W_; ++c) out[c] = v[c];
+    }
+}
+
+// The vector path's whole batches: U steps per wave whose rows all lie below
+// K.  A lane's row pointers into a and b advance by a fixed stride per step
+// (4*W rows), so the batch's loads are issued back to back with one 64-bit
+// add each -- no per-load address multiplies, clamps or selects.  G values of
+// a per lane (a group wholly in or wholly past the end of a's row: M % G ==
+// 0), CW of b.  Returns the first step left to the general loop.  (The 4x4x1
+// kernel keeps the general loop: it measured slower with this one.)
+template <int G, int CW, int W, int U>
+__device__ __forceinline__ int full_batches(const Problem &p, const SliceBase &s, int col, int ia, int wave,
+                                            int kk, floatx4 (&acc)[CW][G]) {
+    const int M = (int)p.M;
+    const int full_steps = (int)(p.K / 4);
+    int base = wave;
+    if (base + (U - 1) * W >= full_steps) return base;
+    const bool a_in = ia < M;
+    const int ic = ia < M - G ? ia : M - G;
+    const int64_t bstride = (int64_t)(4 * W) * p.nb11, astride = (int64_t)(4 * W) * p.nb01;
+    const uint8_t *pb = s.b + (int64_t)(4 * wave + kk) * p.nb11 + (int64_t)col * 4;
+    const uint8_t *pa = s.a + (int64_t)(4 * wave + kk) * p.nb01 + (int64_t)ic * 4;
+    for (; base + (U - 1) * W < full_steps; base += W * U) {
+        float bv[U][CW];
+        float av[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ld_vec<G>(pa + u * astride, av[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) ld_vec<CW>(pb + u * bstride, bv[u]);
+        pa += U * astride;
+        pb += U * bstride;
+        // keep the batch's loads ahead of every use: the scheduler would
+        // otherwise interleave them with the MFMAs, leaving two or three in
+        // flight per wave in a kernel bound by HBM latency
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < G; ++t) av[u][t] = a_in ? av[u][t] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+#pragma unroll
+                for (int t = 0; t < G; ++t)
+                    acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u][c], av[u][t], acc[c][t], 0, 0, 0);
+    }
+    return base;
+}
+
 // The K loop of one wave.  Loads are unconditional (addresses clamped into
 // range, out-of-range values replaced by zero afterwards) so that the U steps'
 // loads are all in flight before the first MFMA waits on them.
@@ -92,7 +151,9 @@ __device__ __forceinline__ void column_k_loop(const Problem &p, const SliceBase 
 #pragma unroll
     for (int t = 0; t < MT; ++t) a_ok[t] = ia + t < M;
     const int steps = (K + 3) / 4;
-    for (int base = wave; base < steps; base += W * U) {
+    int base = wave;
+    if constexpr (FULL) base = full_batches<MT, CW, W, U>(p, s, col, ia, wave, kk, acc);
+    for (; base < steps; base += W * U) {
         float bv[U][CW];
         float av[U][MT];
         // a first: its rows are few and cached, so they arrive before b's
@@ -526,21 +587,25 @@ bool plan_skinny(const Problem &p, Launch *l) {
         if (l->variant > kNumColCfgs) return false;
         cfg = l->variant - 1;
     } else {
-        // measured on MI355X with HBM-resident (cache-cold) inputs, K = 512:
-        // ranks <= 8 over wide b read 256-byte row segments with the 4x4x1
-        // MFMA; narrower b needs more workgroups (16-column strips); wider a
-        // uses the 16x16x4 kernel
-        if (p.M <= 4)
-            cfg = p.N >= 4096 ? 10 : 6;
-        else if (p.M <= 8)
-            cfg = p.N >= 4096 ? 10 : 0;
-        else
+        // measured on MI355X with HBM-resident (cache-cold) inputs, ranks
+        // 4-32, K = 512 / 1024: b up to 4096 columns wide needs 16-column
+        // strips for enough workgroups; up to 16384 columns, 256-byte row
+        // segments (64-column strips) read fastest; wider b, and a with
+        // several 32-column blocks (per-head products), run 32-column strips.
+        // The 4x4x1 kernel is a few % faster for ranks <= 4 over 256-byte
+        // segments and slower everywhere else.
+        if (p.b_kt)
+            cfg = p.M <= 8 ? 6 : 0;  // K-contiguous b: one column per lane
+        else if (p.M > 32)
+            cfg = 1;
+        else if (p.N <= 4096)
             cfg = 0;
+        else if (p.N <= 16384)
+            cfg = p.M <= 4 ? 10 : 2;
+        else
+            cfg = 1;
     }
-    if (p.b_kt && kColCfgs[cfg].cw != 1) {
-        if (l->variant > 0) return false;  // forced wide-strip configuration
-        cfg = p.M <= 8 ? 6 : 0;            // K-contiguous b: one column per lane
-    }
+    if (p.b_kt && kColCfgs[cfg].cw != 1) return false;  // forced wide-strip configuration
     const ColCfg &c = kColCfgs[cfg];
     const int cols = 16 * c.cw;
     const int64_t col_blocks = (p.N + cols - 1) / cols;

@@ -151,7 +151,7 @@ def test_forced_kernels():
     assert B.STATUS[plan(synth.Q8_0, ne, nb, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
     ne, nb = base(a_ne=(33, 512, 1, 1))
     p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_SKINNY)
-    assert p["kernel_name"] == "skinny" and p["tile_m"] == 32 and p["grid"] == 2 * 160
+    assert p["kernel_name"] == "skinny" and p["tile_m"] == 32 and p["tile_n"] == 32 and p["grid"] == 2 * 80
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=7)] == "E_KERNEL"
     for cfg in range(11):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_SKINNY, cfg))
