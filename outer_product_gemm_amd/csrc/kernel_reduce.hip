@@ -24,8 +24,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Problem p, int groups
         const float *src = ws + (int64_t)row * M + i0;
         floatx4 acc;
         if (vec_ws) {
+            // the partials of up to 8 ranges are loaded together (clamped
+            // indices, no branch), then added in range order
             acc = *(const floatx4 *)src;
-            for (int sp = 1; sp < p.splits; ++sp) acc += *(const floatx4 *)(src + sp * split_floats);
+            for (int sp = 1; sp < p.splits; sp += 8) {
+                floatx4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = sp + u < p.splits ? sp + u : p.splits - 1;
+                    v[u] = *(const floatx4 *)(src + r * split_floats);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (sp + u < p.splits) acc += v[u];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
