@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -79,13 +80,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed, so that
+    editing a comment does not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the code (not the comments) of every kernel and host source."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "outer_product_gemm_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update((name + "\n" + _code_only(f.read())).encode())
     return h.hexdigest()[:16]
 
 

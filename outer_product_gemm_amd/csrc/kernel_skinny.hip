@@ -19,7 +19,9 @@
 // c holds the dst columns n0 + CW*i + c.  The W waves take interleaved 4-row
 // steps of K, each wave issuing the loads of U steps together; their partial
 // tiles are summed in LDS in wave order, so the result is deterministic and
-// every dst element has one writer.  No workspace, no atomics.
+// every dst element has one writer.  No atomics; a launch split over K ranges
+// writes each range's partial tile to the stream's workspace instead of dst,
+// and the reduce kernel adds them in range order.
 #include "kernel_common.h"
 #include "outprod.h"
 

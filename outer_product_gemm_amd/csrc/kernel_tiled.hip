@@ -6,8 +6,10 @@
 namespace outprod {
 namespace tiled {
 
-// Rate unit of TileCfg::eff: tile area x K rows per microsecond on one CU
-// (the 27B q4_K shapes: 160 x 128 x 17408 per CU in 1647 us at eff 12.2).
+// Rate unit of TileCfg::eff: tile area x K rows per microsecond on one CU,
+// calibrated on the 27B q4_K shape (160 x 128 x 17408 per CU; 1647 us at eff
+// 12.2 when calibrated, 1550 us since).  Only the ratios between
+// configurations and against the split overheads below matter.
 constexpr double kEffPerUs = 17.7e3;
 // Split-K overheads: the reduce kernel's launch gap and its traffic (every
 // partial read once, dst written once; the main kernel's extra partial writes
