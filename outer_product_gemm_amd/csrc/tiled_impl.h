@@ -611,7 +611,13 @@ struct TileCore {
 
         // MFMA steps [s0, s1) of a stage.  Operand fragments are double-buffered
         // in registers: step st+1's LDS reads are issued before step st's MFMAs.
+        // Column-of-waves tiles (WGM == 1: every wave spans the whole i0
+        // width, 17 MFMA blocks) raise the wave's priority for its MFMA steps,
+        // so a wave ready to feed the matrix core wins issue over one that is
+        // decoding: 3.5% faster there, slower for the other tile shapes.
+        constexpr bool kPrio = WGM == 1;
         auto mfma_steps = [&](int cur, int s0, int s1) {
+            if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
             float af[2][FM], bf[2][FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[0][i] = As[cur][MM::KS * s0 + kq][a_col + MF * i];
@@ -633,6 +639,7 @@ struct TileCore {
                     for (int j = 0; j < FN; ++j)
                         if (!PART || j < fn_act) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
             }
+            if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
         };
         const bool mma = !PART || fn_act > 0;
 
