@@ -51,6 +51,8 @@ def kernel_code(family: int, config: int = None, splits: int = None) -> int:
     return code | (splits << 16 if splits is not None else 0)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
+# The library ABI this binding's structures and signatures match.
+ABI_VERSION = 2
 
 # Every symbol the header declares.
 EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_id_back", "out_prod_id_back_ex",
@@ -79,7 +81,9 @@ _lib = None
 
 
 def load_library(path: str = LIB_PATH):
-    """Load liboutprod.so (once).  Raises if it has not been built."""
+    """Load liboutprod.so (once per process; later calls return the loaded
+    library whatever the path).  Raises if it has not been built or if its
+    ABI version is not the one this binding was written for."""
     global _lib
     with _lock:
         if _lib is None:
@@ -106,6 +110,10 @@ def load_library(path: str = LIB_PATH):
             lib.out_prod_strerror.argtypes = [ctypes.c_int]
             lib.out_prod_strerror.restype = ctypes.c_char_p
             lib.out_prod_version.restype = ctypes.c_int
+            got = int(lib.out_prod_version())
+            if got != ABI_VERSION:
+                raise RuntimeError("%s has ABI version %d, this binding needs %d: rebuild it "
+                                   "(__graft_entry__.build())" % (path, got, ABI_VERSION))
             _lib = lib
     return _lib
 
