@@ -136,10 +136,12 @@ int out_prod(const void *a, int a_type, const float *b, float *dst,
 
 /* Kernel families (for out_prod_plan's report and out_prod_ex's override). */
 #define OUTPROD_KERNEL_AUTO 0   /* let the library choose */
-#define OUTPROD_KERNEL_SKINNY 1 /* f32 a only: MFMA 16x16x4 column kernel, 16 x 16*MT
-                                   dst tiles, K split over the waves of a workgroup; chosen
-                                   for ne00 <= 32 (bandwidth-bound rank-r gradients) and for
-                                   f32 problems with too few output tiles for the tiled kernel */
+#define OUTPROD_KERNEL_SKINNY 1 /* f32 a only: MFMA column kernels (16x16x4, or 16-block
+                                   4x4x1 for narrow a) over strips of 16-64 b columns, K
+                                   spread over the waves of a workgroup (and over workgroups
+                                   when split); chosen for ne00 <= 32 (bandwidth-bound rank-r
+                                   gradients), for a narrow f32 b (operand swap) and for f32
+                                   problems with too few output tiles for the tiled kernel */
 #define OUTPROD_KERNEL_TILED 2  /* LDS-staged fp32 tiles, MFMA 32x32x2 or 16x16x4, any a
                                    type and shape; a menu of tile configurations */
 #define OUTPROD_KERNEL_ZERO 3   /* K == 0: writes zeros */
