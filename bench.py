@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(list(synth.WORKLOADS) + list(synth.MOE_WORKLOADS) + list(COMPOSITE)))
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for 600 MB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU-oracle time for the baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the benchmark: run a plain device copy of MB megabytes "
@@ -405,7 +405,7 @@ def cpu_baseline(insts, sets, target_s):
             f_all += 2 * ne[0] * ne[1] * cnt
             results.append((j, cols, ref, den))
         log("cpu oracle sample: %d columns/launch, %.2f s" % (n, t_all))
-        if t_all >= 0.4 * target_s or n >= 4096:
+        if t_all >= 0.8 * target_s or n >= 4096:
             break
         n = int(n * min(8.0, max(1.5, target_s / max(t_all, 1e-3))))
     total_flops, total_t = f_all, t_all
