@@ -382,11 +382,13 @@ def cpu_baseline(insts, sets, target_s):
     while True:
         t_all, f_all = 0.0, 0
         results = []
+        whole = True   # every launch's sample is its whole output
         for j, inst in enumerate(insts):
             ne = inst.ne
             if is_moe(inst):   # sample routed slots (rows of dst)
                 n_slots = ne[5] * ne[6]
                 cnt = min(n, n_slots)
+                whole = whole and cnt == n_slots
                 sl = np.sort(rng.choice(n_slots, cnt, replace=False))
                 t = time.perf_counter()
                 ref, den = oracle.mul_mat_id_back(inst.a, inst.a_type, inst.g, inst.ids, ne,
@@ -397,6 +399,7 @@ def cpu_baseline(insts, sets, target_s):
                 continue
             slices = ne[10] * ne[11]
             cnt = min(n, ne[4] * slices)
+            whole = whole and cnt == ne[4] * slices
             flat = rng.choice(ne[4] * slices, cnt, replace=False)
             cols = np.array([[c % ne[4], (c // ne[4]) % ne[10], c // (ne[4] * ne[10])] for c in flat])
             t = time.perf_counter()
@@ -405,7 +408,7 @@ def cpu_baseline(insts, sets, target_s):
             f_all += 2 * ne[0] * ne[1] * cnt
             results.append((j, cols, ref, den))
         log("cpu oracle sample: %d columns/launch, %.2f s" % (n, t_all))
-        if t_all >= 0.8 * target_s or n >= 4096:
+        if t_all >= 0.8 * target_s or n >= 4096 or whole:
             break
         n = int(n * min(8.0, max(1.5, target_s / max(t_all, 1e-3))))
     total_flops, total_t = f_all, t_all
