@@ -30,6 +30,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "block_formats.h"
 #include "kernel_common.h"
@@ -45,6 +46,32 @@ namespace tiled {
 // Work is split into groups (4 floats, or 8 quantized values); thread tid
 // takes groups tid, tid+T, ...; the last round is guarded when T does not
 // divide the group count.
+
+// f(integral_constant<int, 0>()), ..., f(integral_constant<int, N-1>()):
+// a loop whose index is a compile-time constant in the body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// Group index of a thread's round: group g = tid + T*j.  With REDO (the
+// full-tile pipelined loop, which has no branches) a thread past the last
+// group of the final round takes a group it already owns, or one another
+// thread owns when there are fewer groups than threads: the same loads and
+// decode, and its LDS write stores the value that is already there.
+template <int G, int T, bool REDO>
+__device__ __forceinline__ int group_index(int g) {
+    if constexpr (!REDO || G % T == 0)
+        return g;
+    else if constexpr (G >= T)
+        return g < G ? g : g - T;
+    else
+        return g < G ? g : g % G;
+}
 
 template <int BW, int BK, int T>
 struct F32Loader {
@@ -69,18 +96,18 @@ struct F32Loader {
     }
     // FULL: the whole tile is in range and 16-byte aligned (uniform,
     // checked by the caller): unconditional vector loads.
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int row = g / (BW / 4), c = w0 + 4 * (g % (BW / 4));
             const int k = k0 + row;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
             if (FULL) {
-                if (kGroups % T == 0 || g < kGroups)
+                if (REDO || kGroups % T == 0 || g < kGroups)
                     v = *(const floatx4 *)(base + (int64_t)k * ld + (int64_t)c * 4);
-            } else if ((kGroups % T == 0 || g < kGroups) && k < K) {
+            } else if ((REDO || kGroups % T == 0 || g < kGroups) && k < K) {
                 const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)c * 4;
                 if (vec && c + 3 < W) {
                     v = *(const floatx4 *)ptr;
@@ -93,12 +120,12 @@ struct F32Loader {
             r[j] = v;
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (kGroups % T == 0 || g < kGroups) {
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (REDO || kGroups % T == 0 || g < kGroups) {
                 const int row = g / (BW / 4), c = 4 * (g % (BW / 4));
                 *(floatx4 *)&lds[row][c] = r[j];
             }
@@ -130,18 +157,18 @@ struct F32LoaderKT {
         vec = vec_ok;
         tid = t;
     }
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int n = g % BW, kq = g / BW;
             const int c = w0 + n, k = k0 + 4 * kq;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
             if (FULL) {
-                if (kGroups % T == 0 || g < kGroups)
+                if (REDO || kGroups % T == 0 || g < kGroups)
                     v = *(const floatx4 *)(base + (int64_t)c * ld + (int64_t)k * 4);
-            } else if ((kGroups % T == 0 || g < kGroups) && c < W) {
+            } else if ((REDO || kGroups % T == 0 || g < kGroups) && c < W) {
                 const uint8_t *ptr = base + (int64_t)c * ld + (int64_t)k * 4;
                 if (vec && k + 3 < K) {
                     v = *(const floatx4 *)ptr;
@@ -154,12 +181,12 @@ struct F32LoaderKT {
             r[j] = v;
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (kGroups % T == 0 || g < kGroups) {
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (REDO || kGroups % T == 0 || g < kGroups) {
                 const int n = g % BW, kq = g / BW;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) lds[4 * kq + e][n] = r[j][e];
@@ -251,16 +278,16 @@ struct Q8Loader {
         m0 = col0;
         tid = t;
     }
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             d[j] = 0;
             q[j][0] = q[j][1] = q[j][2] = q[j][3] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
+            if ((REDO || kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 5) * 34;
                 const uint16_t *qs = (const uint16_t *)(blk + 2 + (m & 31));
                 d[j] = *(const uint16_t *)blk;
@@ -269,12 +296,12 @@ struct Q8Loader {
             }
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (!(kGroups % T == 0 || g < kGroups)) continue;
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (!(REDO || kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             const float dd = half_bits_to_float(d[j]);
             float v[8];
@@ -311,15 +338,15 @@ struct Q4KLoader {
         m0 = col0;
         tid = t;
     }
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             dd[j] = s0[j] = s1[j] = s2[j] = q0[j] = q1[j] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
+            if ((REDO || kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 8) * 144;
                 const int w = m & 255, sub = w >> 5, pos = w & 31;
                 const uint32_t *hdr = (const uint32_t *)blk;
@@ -333,12 +360,12 @@ struct Q4KLoader {
             }
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (!(kGroups % T == 0 || g < kGroups)) continue;
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (!(REDO || kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             const int sub = ((m0 + c) & 255) >> 5;
             // 6-bit scale and min of sub-block `sub` from the 12 packed bytes
@@ -349,15 +376,15 @@ struct Q4KLoader {
             const int sh = 8 * (sub & 3);
             const uint32_t b0 = (s0[j] >> sh) & 0xFFu, b1 = (s1[j] >> sh) & 0xFFu;
             const uint32_t b2 = (s2[j] >> sh) & 0xFFu;
-            const bool hi = sub >= 4;
-            const uint32_t sc = hi ? (b2 & 0x0Fu) | ((b0 >> 6) << 4) : (b0 & 0x3Fu);
-            const uint32_t mn = hi ? (b2 >> 4) | ((b1 >> 6) << 4) : (b1 & 0x3Fu);
+            const uint32_t hm = 0u - (uint32_t)(sub >> 2);  // all ones for sub >= 4
+            const uint32_t sc = (((b2 & 0x0Fu) | ((b0 >> 6) << 4)) & hm) | (b0 & 0x3Fu & ~hm);
+            const uint32_t mn = (((b2 >> 4) | ((b1 >> 6) << 4)) & hm) | (b1 & 0x3Fu & ~hm);
             const float d = half_bits_to_float(dd[j] & 0xFFFFu);
             const float dmin = half_bits_to_float(dd[j] >> 16);
             const float ds = d * (float)sc;    // exact: <= 17 significant bits
             const float dm = dmin * (float)mn; // exact
             // this sub-block's nibble of each of the 8 code bytes, as bytes
-            const int shift = (sub & 1) ? 4 : 0;
+            const int shift = 4 * (sub & 1);
             const uint32_t n0 = (q0[j] >> shift) & 0x0F0F0F0Fu, n1 = (q1[j] >> shift) & 0x0F0F0F0Fu;
             float v[8];
 #pragma unroll
@@ -397,15 +424,15 @@ struct HalfLoader {
         vec = vec_ok;
         tid = t;
     }
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
             r[j][0] = r[j][1] = r[j][2] = r[j][3] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
+            if ((REDO || kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *ptr = base + (int64_t)k * ld + (int64_t)m * 2;
                 if (FULL || (vec && m + 7 < M)) {
                     const uint4 q = *(const uint4 *)ptr;
@@ -421,12 +448,12 @@ struct HalfLoader {
             }
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (!(kGroups % T == 0 || g < kGroups)) continue;
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (!(REDO || kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             float v[8];
 #pragma unroll
@@ -461,27 +488,27 @@ struct BlockLoader {
         m0 = col0;
         tid = t;
     }
-    template <bool FULL>
+    template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
             const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
             const int k = k0 + row;
 #pragma unroll
             for (int x = 0; x < F::NW; ++x) r[j][x] = 0;
-            if ((kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
+            if ((REDO || kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m / F::QK) * F::BYTES;
                 F::fetch(blk, m % F::QK, r[j]);
             }
         }
     }
-    template <int LD>
+    template <int LD, bool REDO = false, int J0 = 0, int J1 = kPer>
     __device__ void store(float (*lds)[LD]) const {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int g = tid + T * j;
-            if (!(kGroups % T == 0 || g < kGroups)) continue;
+        for (int j = J0; j < J1; ++j) {
+            const int g = group_index<kGroups, T, REDO>(tid + T * j);
+            if (!(REDO || kGroups % T == 0 || g < kGroups)) continue;
             const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
             float v[8];
             F::decode(r[j], (m0 + c) % F::QK, v);
@@ -661,6 +688,127 @@ struct TileCore {
         }
     }
 
+    // Full tiles (every load in range, K a whole number of stages): the same
+    // contraction as run<true>, summed in the same order, by a stage loop
+    // without branches.  Two register sets hold the raw operand data of the
+    // next two stages, so a stage's global loads are issued two stages before
+    // they are decoded; stage t+1's decode into the free LDS buffer and the
+    // loads of stage t+3 are spread over stage t's MFMA steps (one a group
+    // per step, then the b tile, then the loads), where the matrix core has
+    // work queued while the wave decodes.
+    template <class LA, class LB>
+    __device__ static void run_pipe(LA (&la)[2], LB (&lb)[2], int K, float (&As)[2][BK][LDA],
+                                    float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN]) {
+        static_assert(LA::kPer + 2 <= S, "a stage has too few MFMA steps for its decode");
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave % WGM, wn = wave / WGM;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
+        const int kq = lane / MF, col = lane % MF;
+        const int a_col = wm * WTM + col, b_col = wn * WTN + col;
+        // a's last round: when its groups fill whole waves, the waves past
+        // them skip it (a scalar branch) instead of decoding a group again
+        constexpr int kTailGroups = LA::kGroups - T * (LA::kPer - 1);
+        constexpr bool kTailWave = LA::kGroups % T != 0 && kTailGroups % 64 == 0;
+        const bool tail_on = __builtin_amdgcn_readfirstlane(wave) * 64 < kTailGroups;
+
+        // One stage: the MFMA steps on LDS buffer `cur`; with DEC, the
+        // decode of register set (xa, xb) into buffer cur^1; with LOAD, then
+        // the loads of rows [kload, kload + BK) into that set.
+        auto stage = [&](auto dec_c, auto load_c, int cur, LA &xa, LB &xb, int kload) {
+            constexpr bool DEC = decltype(dec_c)::value, LOAD = decltype(load_c)::value;
+            float af[2][FM], bf[2][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[0][i] = As[cur][kq][a_col + MF * i];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][kq][b_col + MF * j];
+            static_for<S>([&](auto st_c) {
+                constexpr int st = decltype(st_c)::value, x = st & 1;
+                if constexpr (st + 1 < S) {
+                    const int kr = MM::KS * (st + 1) + kq;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
+                }
+                auto mfmas = [&]() {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
+                };
+                // chunk c of the decode work (a group c < kPer, then the b
+                // tile, then the loads) runs in step c * S / (kPer + 2)
+                constexpr int NC = LA::kPer + 2;
+                constexpr int c = (st * NC + S - 1) / S;  // first chunk at or after this step
+                constexpr bool here = DEC && c < NC && c * S / NC == st;
+                if constexpr (here && c == LA::kPer - 1 && kTailWave) {
+                    // the last a round has groups only in the first waves:
+                    // a wave-uniform branch, MFMAs on both sides
+                    if (tail_on) {
+                        mfmas();
+                        xa.template store<LDA, true, c, c + 1>(As[cur ^ 1]);
+                    } else {
+                        mfmas();
+                    }
+                } else {
+                    mfmas();
+                    if constexpr (here && c < LA::kPer) {
+                        xa.template store<LDA, true, c, c + 1>(As[cur ^ 1]);
+                    } else if constexpr (here && c == LA::kPer) {
+                        xb.template store<LDB, true>(Bs[cur ^ 1]);
+                    } else if constexpr (here && c == LA::kPer + 1 && LOAD) {
+                        xa.template load<true, true>(kload);
+                        xb.template load<true, true>(kload);
+                    }
+                }
+            });
+        };
+        typedef std::integral_constant<bool, true> Y;
+        typedef std::integral_constant<bool, false> N;
+
+        const int ktiles = K / BK;
+        la[0].template load<true, true>(0);
+        lb[0].template load<true, true>(0);
+        if (ktiles > 1) {
+            la[1].template load<true, true>(BK);
+            lb[1].template load<true, true>(BK);
+        }
+        la[0].template store<LDA, true>(As[0]);
+        lb[0].template store<LDB, true>(Bs[0]);
+        if (ktiles > 2) {
+            la[0].template load<true, true>(2 * BK);
+            lb[0].template load<true, true>(2 * BK);
+        }
+        __syncthreads();
+        int t = 0;
+        // steady state: stage t decodes set 1 (stage t+1) and loads stage t+3
+        // into it; stage t+1 decodes set 0 (stage t+2) and loads stage t+4
+        for (; t + 4 < ktiles; t += 2) {
+            stage(Y(), Y(), 0, la[1], lb[1], (t + 3) * BK);
+            __syncthreads();
+            stage(Y(), Y(), 1, la[0], lb[0], (t + 4) * BK);
+            __syncthreads();
+        }
+        for (; t < ktiles; ++t) {
+            const bool dec = t + 1 < ktiles, ld = t + 3 < ktiles;
+            if (t & 1) {
+                if (ld) stage(Y(), Y(), 1, la[0], lb[0], (t + 3) * BK);
+                else if (dec) stage(Y(), N(), 1, la[0], lb[0], 0);
+                else stage(N(), N(), 1, la[0], lb[0], 0);
+            } else {
+                if (ld) stage(Y(), Y(), 0, la[1], lb[1], (t + 3) * BK);
+                else if (dec) stage(Y(), N(), 0, la[1], lb[1], 0);
+                else stage(N(), N(), 0, la[1], lb[1], 0);
+            }
+            __syncthreads();
+        }
+    }
+
     // Tile-relative dst position of accumulator (i, j, register r) of this
     // lane: column (along i0) and row (along i1).
     __device__ static int col_of(int i) {
@@ -706,10 +854,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
                           p.vec_a;
     const bool full = m0 + BM <= M && n0 + BN <= N && K % BK == 0 && a_vec_ok && p.vec_b;
     typename C::acc_t acc[FM][FN];
-    if (full)
-        C::template run<true>(la, lb, K, As, Bs, acc);
-    else
+    typedef decltype(la) LA;
+    typedef decltype(lb) LB;
+    // the pipelined loop needs a step per a group plus two, and registers
+    // for two raw stages next to the accumulators (the column-of-waves tiles,
+    // 17 accumulator blocks per wave, only with 16-row stages)
+    constexpr bool kPipe = LA::kPer + 2 <= C::S && (WGM > 1 || BK == 16);
+    if (full) {
+        if constexpr (kPipe) {
+            LA la2[2] = {la, la};
+            LB lb2[2] = {lb, lb};
+            C::run_pipe(la2, lb2, K, As, Bs, acc);
+        } else {
+            C::template run<true>(la, lb, K, As, Bs, acc);
+        }
+    } else {
         C::template run<false>(la, lb, K, As, Bs, acc);
+    }
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
