@@ -56,7 +56,7 @@ struct FmtQ4_0 {
     __device__ static void decode(const uint32_t (&r)[NW], int w, float (&v)[8]) {
         const float d = half_bits_to_float(r[0]), off = -8.f * d;  // exact
         const int sh = w >= 16 ? 4 : 0;
-        const uint32_t n0 = (r[1] >> sh) & 0x0F0F0F0Fu, n1 = (r[2] >> sh) & 0x0F0F0F0Fu;
+        const uint32_t n0 = opaque((r[1] >> sh) & 0x0F0F0F0Fu), n1 = opaque((r[2] >> sh) & 0x0F0F0F0Fu);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // d*q - 8d = d*(q - 8): exact (<= 15 significant bits)
@@ -77,7 +77,7 @@ struct FmtQ4_1 {
     __device__ static void decode(const uint32_t (&r)[NW], int w, float (&v)[8]) {
         const float d = half_bits_to_float(r[0] & 0xFFFFu), m = half_bits_to_float(r[0] >> 16);
         const int sh = w >= 16 ? 4 : 0;
-        const uint32_t n0 = (r[1] >> sh) & 0x0F0F0F0Fu, n1 = (r[2] >> sh) & 0x0F0F0F0Fu;
+        const uint32_t n0 = opaque((r[1] >> sh) & 0x0F0F0F0Fu), n1 = opaque((r[2] >> sh) & 0x0F0F0F0Fu);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // d*q exact, one rounding with + m
             v[e] = __builtin_fmaf(d, ubyte(n0, e), m);
@@ -100,8 +100,8 @@ struct FmtQ5_0 {
         const float d = half_bits_to_float(r[0]), off = -16.f * d;  // exact
         const int sh = w >= 16 ? 4 : 0;
         const uint32_t hb = (r[1] >> (8 * ((w >> 3) & 1))) & 0xFFu;
-        const uint32_t n0 = ((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4);
-        const uint32_t n1 = ((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4);
+        const uint32_t n0 = opaque(((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4));
+        const uint32_t n1 = opaque(((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // d*(q - 16): exact
             v[e] = __builtin_fmaf(d, ubyte(n0, e), off);
@@ -123,8 +123,8 @@ struct FmtQ5_1 {
         const float d = half_bits_to_float(r[0] & 0xFFFFu), m = half_bits_to_float(r[0] >> 16);
         const int sh = w >= 16 ? 4 : 0;
         const uint32_t hb = (r[1] >> w) & 0xFFu;
-        const uint32_t n0 = ((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4);
-        const uint32_t n1 = ((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4);
+        const uint32_t n0 = opaque(((r[2] >> sh) & 0x0F0F0F0Fu) | (spread4(hb) << 4));
+        const uint32_t n1 = opaque(((r[3] >> sh) & 0x0F0F0F0Fu) | (spread4(hb >> 4) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // d*q exact, one rounding with + m
             v[e] = __builtin_fmaf(d, ubyte(n0, e), m);
@@ -150,7 +150,7 @@ struct FmtQ2_K {
         const uint32_t sm = (r[1] >> (8 * ((w >> 4) & 3))) & 0xFFu;
         const float ds = d * (float)(sm & 0xFu), dm = dmin * (float)(sm >> 4);
         const int sh = 2 * ((w >> 5) & 3);
-        const uint32_t n0 = (r[2] >> sh) & 0x03030303u, n1 = (r[3] >> sh) & 0x03030303u;
+        const uint32_t n0 = opaque((r[2] >> sh) & 0x03030303u), n1 = opaque((r[3] >> sh) & 0x03030303u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // ds*q exact, one rounding with - dm
             v[e] = __builtin_fmaf(ds, ubyte(n0, e), -dm);
@@ -185,8 +185,8 @@ struct FmtQ3_K {
         const float dl = half_bits_to_float(r[0]) * (float)((int)(lo4 | (hi2 << 4)) - 32);
         const int hs = 4 * h + j;
         // u = low | keep << 2 in each byte; q = u - 4 (keep set: q = low)
-        const uint32_t u0 = ((r[3] >> (2 * j)) & 0x03030303u) | (((r[1] >> hs) & 0x01010101u) << 2);
-        const uint32_t u1 = ((r[4] >> (2 * j)) & 0x03030303u) | (((r[2] >> hs) & 0x01010101u) << 2);
+        const uint32_t u0 = opaque(((r[3] >> (2 * j)) & 0x03030303u) | (((r[1] >> hs) & 0x01010101u) << 2));
+        const uint32_t u1 = opaque(((r[4] >> (2 * j)) & 0x03030303u) | (((r[2] >> hs) & 0x01010101u) << 2));
         const float off = -4.f * dl;  // exact
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // dl*(u - 4): exact
@@ -236,8 +236,8 @@ struct FmtQ5_K {
         const float ds = half_bits_to_float(r[0] & 0xFFFFu) * (float)sc;
         const float dm = half_bits_to_float(r[0] >> 16) * (float)mn;
         const int hs = 2 * g + s;
-        const uint32_t n0 = ((r[6] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[4] >> hs) & 0x01010101u) << 4);
-        const uint32_t n1 = ((r[7] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[5] >> hs) & 0x01010101u) << 4);
+        const uint32_t n0 = opaque(((r[6] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[4] >> hs) & 0x01010101u) << 4));
+        const uint32_t n1 = opaque(((r[7] >> (4 * s)) & 0x0F0F0F0Fu) | (((r[5] >> hs) & 0x01010101u) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // ds*q exact, one rounding with - dm
             v[e] = __builtin_fmaf(ds, ubyte(n0, e), -dm);
@@ -267,8 +267,8 @@ struct FmtQ6_K {
         const int sc = (int)(int8_t)((r[5] >> (8 * ((w >> 4) & 1))) & 0xFFu);
         const float ds = half_bits_to_float(r[0]) * (float)sc;  // exact: <= 19 bits
         const int ns = 4 * (c >> 1);
-        const uint32_t u0 = ((r[1] >> ns) & 0x0F0F0F0Fu) | (((r[3] >> (2 * c)) & 0x03030303u) << 4);
-        const uint32_t u1 = ((r[2] >> ns) & 0x0F0F0F0Fu) | (((r[4] >> (2 * c)) & 0x03030303u) << 4);
+        const uint32_t u0 = opaque(((r[1] >> ns) & 0x0F0F0F0Fu) | (((r[3] >> (2 * c)) & 0x03030303u) << 4));
+        const uint32_t u1 = opaque(((r[2] >> ns) & 0x0F0F0F0Fu) | (((r[4] >> (2 * c)) & 0x03030303u) << 4));
         const float off = -32.f * ds;  // exact
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // ds*(u - 32) rounded once, as d*scale*q

@@ -77,4 +77,13 @@ __device__ __forceinline__ void apply_split(Problem &q, SliceBase &s, int z, int
 
 __device__ __forceinline__ float ldf(const uint8_t *p) { return *(const float *)p; }
 
+// x, hidden from the optimizer's known-bits analysis (an empty asm with x as
+// its in/out operand; no instruction is emitted).  For a dword of masked
+// codes it keeps byte e's conversion a single v_cvt_f32_ubyte{e} instead of a
+// bit-field extract of the known-nonzero bits plus a conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
 }  // namespace outprod

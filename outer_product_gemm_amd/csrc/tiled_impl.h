@@ -372,20 +372,23 @@ struct Q4KLoader {
             // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2), without branches: for
             // sub < 4 the low 6 bits of bytes sub and 4+sub; otherwise the
             // nibbles of byte 8+(sub-4) below the top two bits of bytes sub-4
-            // and sub.
-            const int sh = 8 * (sub & 3);
-            const uint32_t b0 = (s0[j] >> sh) & 0xFFu, b1 = (s1[j] >> sh) & 0xFFu;
-            const uint32_t b2 = (s2[j] >> sh) & 0xFFu;
-            const uint32_t hm = 0u - (uint32_t)(sub >> 2);  // all ones for sub >= 4
-            const uint32_t sc = (((b2 & 0x0Fu) | ((b0 >> 6) << 4)) & hm) | (b0 & 0x3Fu & ~hm);
-            const uint32_t mn = (((b2 >> 4) | ((b1 >> 6) << 4)) & hm) | (b1 & 0x3Fu & ~hm);
+            // and sub.  Bit-field extracts with per-lane offsets and widths
+            // (the top bits' width is 0 for sub < 4, which extracts 0).
+            const uint32_t sh = 8 * (sub & 3);
+            const bool hi = sub >= 4;
+            const uint32_t w_lo = hi ? 4u : 6u, w_top = hi ? 2u : 0u;
+            const uint32_t sc = __builtin_amdgcn_ubfe(hi ? s2[j] : s0[j], sh, w_lo) |
+                                (__builtin_amdgcn_ubfe(s0[j], sh + 6, w_top) << 4);
+            const uint32_t mn = __builtin_amdgcn_ubfe(hi ? s2[j] : s1[j], hi ? sh + 4 : sh, w_lo) |
+                                (__builtin_amdgcn_ubfe(s1[j], sh + 6, w_top) << 4);
             const float d = half_bits_to_float(dd[j] & 0xFFFFu);
             const float dmin = half_bits_to_float(dd[j] >> 16);
             const float ds = d * (float)sc;    // exact: <= 17 significant bits
             const float dm = dmin * (float)mn; // exact
             // this sub-block's nibble of each of the 8 code bytes, as bytes
             const int shift = 4 * (sub & 1);
-            const uint32_t n0 = (q0[j] >> shift) & 0x0F0F0F0Fu, n1 = (q1[j] >> shift) & 0x0F0F0F0Fu;
+            const uint32_t n0 = opaque((q0[j] >> shift) & 0x0F0F0F0Fu);
+            const uint32_t n1 = opaque((q1[j] >> shift) & 0x0F0F0F0Fu);
             float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
