@@ -318,16 +318,18 @@ struct Q8Loader {
     }
 };
 
-// q4_K a: groups of 8 consecutive values of one 32-value sub-block.
-template <int BM, int BK, int T>
+// q4_K a: groups of GV (8 or 16) consecutive values of one 32-value
+// sub-block; a group's scale and min are decoded once for its GV values.
+template <int BM, int BK, int T, int GV>
 struct Q4KLoader {
-    static constexpr int kGroups = BK * BM / 8;
+    static constexpr int kGroups = BK * BM / GV;
     static constexpr int kPer = (kGroups + T - 1) / T;
-    static_assert(BM % 8 == 0, "tile width must be a multiple of 8");
+    static constexpr int NQ = GV / 4;  // code dwords per group
+    static_assert(BM % GV == 0 && (GV == 8 || GV == 16), "tile width must be a multiple of the group");
     const uint8_t *base;
     int64_t ld;
     int m0, M, K, tid;
-    uint32_t dd[kPer], s0[kPer], s1[kPer], s2[kPer], q0[kPer], q1[kPer];
+    uint32_t dd[kPer], s0[kPer], s1[kPer], s2[kPer], q[kPer][NQ];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool, int t) {
@@ -343,9 +345,11 @@ struct Q4KLoader {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
-            const int row = g / (BM / 8), m = m0 + 8 * (g % (BM / 8));
+            const int row = g / (BM / GV), m = m0 + GV * (g % (BM / GV));
             const int k = k0 + row;
-            dd[j] = s0[j] = s1[j] = s2[j] = q0[j] = q1[j] = 0;
+            dd[j] = s0[j] = s1[j] = s2[j] = 0;
+#pragma unroll
+            for (int e = 0; e < NQ; ++e) q[j][e] = 0;
             if ((REDO || kGroups % T == 0 || g < kGroups) && (FULL || (k < K && m < M))) {
                 const uint8_t *blk = base + (int64_t)k * ld + (int64_t)(m >> 8) * 144;
                 const int w = m & 255, sub = w >> 5, pos = w & 31;
@@ -355,8 +359,8 @@ struct Q4KLoader {
                 s0[j] = hdr[1];
                 s1[j] = hdr[2];
                 s2[j] = hdr[3];
-                q0[j] = qs[0];
-                q1[j] = qs[1];
+#pragma unroll
+                for (int e = 0; e < NQ; ++e) q[j][e] = qs[e];
             }
         }
     }
@@ -366,7 +370,7 @@ struct Q4KLoader {
         for (int j = J0; j < J1; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
             if (!(REDO || kGroups % T == 0 || g < kGroups)) continue;
-            const int row = g / (BM / 8), c = 8 * (g % (BM / 8));
+            const int row = g / (BM / GV), c = GV * (g % (BM / GV));
             const int sub = ((m0 + c) & 255) >> 5;
             // 6-bit scale and min of sub-block `sub` from the 12 packed bytes
             // (bytes 0-3 in s0, 4-7 in s1, 8-11 in s2), without branches: for
@@ -385,19 +389,16 @@ struct Q4KLoader {
             const float dmin = half_bits_to_float(dd[j] >> 16);
             const float ds = d * (float)sc;    // exact: <= 17 significant bits
             const float dm = dmin * (float)mn; // exact
-            // this sub-block's nibble of each of the 8 code bytes, as bytes
+            // this sub-block's nibble of each code byte, as bytes
             const int shift = 4 * (sub & 1);
-            const uint32_t n0 = opaque((q0[j] >> shift) & 0x0F0F0F0Fu);
-            const uint32_t n1 = opaque((q1[j] >> shift) & 0x0F0F0F0Fu);
-            float v[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < NQ; ++e) {
+                const uint32_t n = opaque((q[j][e] >> shift) & 0x0F0F0F0Fu);
                 // value = d*sc*q - dmin*m: the product is exact, one rounding
-                v[e] = ds * (float)((n0 >> (8 * e)) & 0xFFu) - dm;
-                v[4 + e] = ds * (float)((n1 >> (8 * e)) & 0xFFu) - dm;
+                *(floatx4 *)&lds[row][c + 4 * e] =
+                    floatx4{ds * (float)(n & 0xFFu) - dm, ds * (float)((n >> 8) & 0xFFu) - dm,
+                            ds * (float)((n >> 16) & 0xFFu) - dm, ds * (float)(n >> 24) - dm};
             }
-            *(floatx4 *)&lds[row][c] = floatx4{v[0], v[1], v[2], v[3]};
-            *(floatx4 *)&lds[row][c + 4] = floatx4{v[4], v[5], v[6], v[7]};
         }
     }
 };
@@ -521,32 +522,36 @@ struct BlockLoader {
     }
 };
 
-template <int AT, int BM, int BK, int T>
+// a's loader for a type.  WIDE: the tile runs the pipelined full-tile loop,
+// where q4_K decodes groups of 16 values (one scale/min decode per 16); the
+// checked loop keeps groups of 8, whose tail round is spread more evenly
+// over the waves.
+template <int AT, int BM, int BK, int T, bool WIDE = false>
 struct ALoaderFor;
-template <int BM, int BK, int T>
-struct ALoaderFor<OUTPROD_TYPE_F32, BM, BK, T> {
+template <int BM, int BK, int T, bool WIDE>
+struct ALoaderFor<OUTPROD_TYPE_F32, BM, BK, T, WIDE> {
     typedef F32Loader<BM, BK, T> type;
 };
-template <int BM, int BK, int T>
-struct ALoaderFor<OUTPROD_TYPE_Q8_0, BM, BK, T> {
+template <int BM, int BK, int T, bool WIDE>
+struct ALoaderFor<OUTPROD_TYPE_Q8_0, BM, BK, T, WIDE> {
     typedef Q8Loader<BM, BK, T> type;
 };
-template <int BM, int BK, int T>
-struct ALoaderFor<OUTPROD_TYPE_Q4_K, BM, BK, T> {
-    typedef Q4KLoader<BM, BK, T> type;
+template <int BM, int BK, int T, bool WIDE>
+struct ALoaderFor<OUTPROD_TYPE_Q4_K, BM, BK, T, WIDE> {
+    typedef Q4KLoader<BM, BK, T, WIDE ? 16 : 8> type;
 };
 
-template <int BM, int BK, int T>
-struct ALoaderFor<OUTPROD_TYPE_F16, BM, BK, T> {
+template <int BM, int BK, int T, bool WIDE>
+struct ALoaderFor<OUTPROD_TYPE_F16, BM, BK, T, WIDE> {
     typedef HalfLoader<false, BM, BK, T> type;
 };
-template <int BM, int BK, int T>
-struct ALoaderFor<OUTPROD_TYPE_BF16, BM, BK, T> {
+template <int BM, int BK, int T, bool WIDE>
+struct ALoaderFor<OUTPROD_TYPE_BF16, BM, BK, T, WIDE> {
     typedef HalfLoader<true, BM, BK, T> type;
 };
 #define OUTPROD_BLOCK_LOADER(TYPE, FMT)                  \
-    template <int BM, int BK, int T>                     \
-    struct ALoaderFor<TYPE, BM, BK, T> {                 \
+    template <int BM, int BK, int T, bool WIDE>          \
+    struct ALoaderFor<TYPE, BM, BK, T, WIDE> {           \
         typedef BlockLoader<FMT, BM, BK, T> type;        \
     };
 OUTPROD_BLOCK_LOADER(OUTPROD_TYPE_Q4_0, FmtQ4_0)
@@ -846,7 +851,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     if (p.splits > 1) apply_split(p, s, z, sp);
     const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
 
-    typename ALoaderFor<AT, BM, BK, T>::type la;
+    // the pipelined loop needs registers for two raw stages next to the
+    // accumulators (the column-of-waves tiles, 17 accumulator blocks per
+    // wave, only with 16-row stages) and a step per a group plus two
+    constexpr bool kPipeCfg = WGM > 1 || BK == 16;
+    typename ALoaderFor<AT, BM, BK, T, kPipeCfg>::type la;
     typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
@@ -859,10 +868,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     typename C::acc_t acc[FM][FN];
     typedef decltype(la) LA;
     typedef decltype(lb) LB;
-    // the pipelined loop needs a step per a group plus two, and registers
-    // for two raw stages next to the accumulators (the column-of-waves tiles,
-    // 17 accumulator blocks per wave, only with 16-row stages)
-    constexpr bool kPipe = LA::kPer + 2 <= C::S && (WGM > 1 || BK == 16);
+    constexpr bool kPipe = kPipeCfg && LA::kPer + 2 <= C::S;
     if (full) {
         if constexpr (kPipe) {
             LA la2[2] = {la, la};
