@@ -73,7 +73,19 @@ __device__ __forceinline__ int group_index(int g) {
         return g < G ? g : g % G;
 }
 
-template <int BW, int BK, int T>
+// Column swizzle of the b tile in LDS: row k of a tile whose width is a
+// multiple of 64 stores column n at n ^ (((k / 4) % 4) * 16), a permutation
+// of 16-column blocks within each 64-column group.  The transposing loaders
+// then write 4 consecutive k of 16 columns into 64 different banks, and the
+// MFMA operand reads (16 or 32 consecutive columns of rows that share k / 4)
+// stay contiguous.  Narrower tiles (80 rows) are stored unswizzled.
+template <int BW>
+__device__ __forceinline__ constexpr int b_swizzle(int k) {
+    return BW % 64 == 0 ? ((k >> 2) & 3) << 4 : 0;
+}
+
+// f32 rows.  SWZ: the tile is b's, stored with b_swizzle.
+template <int BW, int BK, int T, bool SWZ = false>
 struct F32Loader {
     static constexpr int kGroups = BK * BW / 4;
     static constexpr int kPer = (kGroups + T - 1) / T;
@@ -127,7 +139,7 @@ struct F32Loader {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
             if (REDO || kGroups % T == 0 || g < kGroups) {
                 const int row = g / (BW / 4), c = 4 * (g % (BW / 4));
-                *(floatx4 *)&lds[row][c] = r[j];
+                *(floatx4 *)&lds[row][SWZ ? c ^ b_swizzle<BW>(row) : c] = r[j];
             }
         }
     }
@@ -135,17 +147,24 @@ struct F32Loader {
 
 // f32 b whose K dim is contiguous (a transposed view; column stride `ld`):
 // groups of 4 consecutive k of one column, written transposed into the same
-// [k][column] LDS tile.
+// [k][column] LDS tile (with b_swizzle).  Four consecutive groups are the 16
+// consecutive k (64 bytes) of one column, so a wave's load covers 16 columns
+// in whole 64-byte segments.
 template <int BW, int BK, int T>
 struct F32LoaderKT {
     static constexpr int kGroups = BK / 4 * BW;
     static constexpr int kPer = (kGroups + T - 1) / T;
     static_assert(BK % 4 == 0, "stage rows must be a multiple of 4");
+    static constexpr int KQ = BK / 4 < 4 ? BK / 4 : 4;  // k groups per column segment
     const uint8_t *base;
     int64_t ld;
     int w0, W, K, tid;
     bool vec;
     floatx4 r[kPer];
+
+    // group g -> column n and group of 4 rows kq of the stage
+    __device__ static int col_of(int g) { return (g / KQ) % BW; }
+    __device__ static int kq_of(int g) { return g % KQ + KQ * (g / (KQ * BW)); }
 
     __device__ void init(const uint8_t *slice, int64_t col_stride, int width, int k_len,
                          int col0, bool vec_ok, int t) {
@@ -162,7 +181,7 @@ struct F32LoaderKT {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
-            const int n = g % BW, kq = g / BW;
+            const int n = col_of(g), kq = kq_of(g);
             const int c = w0 + n, k = k0 + 4 * kq;
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
             if (FULL) {
@@ -187,9 +206,10 @@ struct F32LoaderKT {
         for (int j = J0; j < J1; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
             if (REDO || kGroups % T == 0 || g < kGroups) {
-                const int n = g % BW, kq = g / BW;
+                const int n = col_of(g), kq = kq_of(g);
+                const int sn = n ^ b_swizzle<BW>(4 * kq);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lds[4 * kq + e][n] = r[j][e];
+                for (int e = 0; e < 4; ++e) lds[4 * kq + e][sn] = r[j][e];
             }
         }
     }
@@ -198,17 +218,23 @@ struct F32LoaderKT {
 // f32 b columns gathered from anywhere (the routed slots of one expert in
 // MUL_MAT_ID_BACK): column n of the tile starts at cols[n] (nullptr: no
 // column) and holds K contiguous floats; groups of 4 consecutive k written
-// transposed into the [k][column] LDS tile.  vec: every column start is
-// 16-byte aligned.
+// transposed into the [k][column] LDS tile (with b_swizzle), four
+// consecutive groups covering 16 consecutive k of one column.  vec: every
+// column start is 16-byte aligned.
 template <int BW, int BK, int T>
 struct GatherLoaderKT {
     static constexpr int kGroups = BK / 4 * BW;
     static constexpr int kPer = (kGroups + T - 1) / T;
     static_assert(BK % 4 == 0, "stage rows must be a multiple of 4");
+    static constexpr int KQ = BK / 4 < 4 ? BK / 4 : 4;
     const uint8_t *col[kPer];
     int K, tid;
     bool vec;
     floatx4 r[kPer];
+
+    // group g -> column n and group of 4 rows kq (as F32LoaderKT)
+    __device__ static int col_of(int g) { return (g / KQ) % BW; }
+    __device__ static int kq_of(int g) { return g % KQ + KQ * (g / (KQ * BW)); }
 
     __device__ void init(const uint8_t *const *cols, int k_len, bool vec_ok, int t) {
         K = k_len;
@@ -217,7 +243,7 @@ struct GatherLoaderKT {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
-            col[j] = (kGroups % T == 0 || g < kGroups) ? cols[g % BW] : nullptr;
+            col[j] = (kGroups % T == 0 || g < kGroups) ? cols[col_of(g)] : nullptr;
         }
     }
     template <bool FULL>
@@ -225,7 +251,7 @@ struct GatherLoaderKT {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
-            const int k = k0 + 4 * (g / BW);
+            const int k = k0 + 4 * kq_of(g);
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
             if (FULL) {
                 if (kGroups % T == 0 || g < kGroups) v = *(const floatx4 *)(col[j] + (int64_t)k * 4);
@@ -248,9 +274,10 @@ struct GatherLoaderKT {
         for (int j = 0; j < kPer; ++j) {
             const int g = tid + T * j;
             if (kGroups % T == 0 || g < kGroups) {
-                const int n = g % BW, kq = g / BW;
+                const int n = col_of(g), kq = kq_of(g);
+                const int sn = n ^ b_swizzle<BW>(4 * kq);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lds[4 * kq + e][n] = r[j][e];
+                for (int e = 0; e < 4; ++e) lds[4 * kq + e][sn] = r[j][e];
             }
         }
     }
@@ -657,7 +684,8 @@ struct TileCore {
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[0][i] = As[cur][MM::KS * s0 + kq][a_col + MF * i];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][MM::KS * s0 + kq][b_col + MF * j];
+            for (int j = 0; j < FN; ++j)
+                bf[0][j] = Bs[cur][MM::KS * s0 + kq][(b_col + MF * j) ^ b_swizzle<BN>(MM::KS * s0)];
 #pragma unroll
             for (int st = s0; st < s1; ++st) {
                 const int x = (st - s0) & 1;
@@ -666,7 +694,8 @@ struct TileCore {
 #pragma unroll
                     for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
+                    for (int j = 0; j < FN; ++j)
+                        bf[x ^ 1][j] = Bs[cur][kr][(b_col + MF * j) ^ b_swizzle<BN>(MM::KS * (st + 1))];
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
@@ -733,7 +762,7 @@ struct TileCore {
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[0][i] = As[cur][kq][a_col + MF * i];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][kq][b_col + MF * j];
+            for (int j = 0; j < FN; ++j) bf[0][j] = Bs[cur][kq][(b_col + MF * j) ^ b_swizzle<BN>(0)];
             static_for<S>([&](auto st_c) {
                 constexpr int st = decltype(st_c)::value, x = st & 1;
                 if constexpr (st + 1 < S) {
@@ -741,7 +770,8 @@ struct TileCore {
 #pragma unroll
                     for (int i = 0; i < FM; ++i) af[x ^ 1][i] = As[cur][kr][a_col + MF * i];
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) bf[x ^ 1][j] = Bs[cur][kr][b_col + MF * j];
+                    for (int j = 0; j < FN; ++j)
+                        bf[x ^ 1][j] = Bs[cur][kr][(b_col + MF * j) ^ b_swizzle<BN>(MM::KS * (st + 1))];
                 }
                 auto mfmas = [&]() {
 #pragma unroll
@@ -856,7 +886,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     // wave, only with 16-row stages) and a step per a group plus two
     constexpr bool kPipeCfg = WGM > 1 || BK == 16;
     typename ALoaderFor<AT, BM, BK, T, kPipeCfg>::type la;
-    typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T>>::type lb;
+    typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T, true>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
 
