@@ -882,9 +882,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
 
     // the pipelined loop needs registers for two raw stages next to the
-    // accumulators (the column-of-waves tiles, 17 accumulator blocks per
-    // wave, only with 16-row stages) and a step per a group plus two
-    constexpr bool kPipeCfg = WGM > 1 || BK == 16;
+    // accumulators (not the column-of-waves tiles: with 17 accumulator blocks
+    // per wave they spill) and a step per a group plus two
+    constexpr bool kPipeCfg = WGM > 1;
     typename ALoaderFor<AT, BM, BK, T, kPipeCfg>::type la;
     typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T, true>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
