@@ -18,12 +18,15 @@
 //   to fp32;
 //   b: f32) -> LDS [k][i0] / [k][i1] (fp32, two buffers) ->
 //   v_mfma_f32_{32x32x2,16x16x4}_f32 with fp32 accumulators.
-// Pipeline: the registers hold stage t+1 while stage t is multiplied; halfway
-// through stage t's MFMAs they are decoded into the other LDS buffer and the
-// loads of stage t+2 are issued, so a global load has a whole stage of matrix
-// work to arrive.  One barrier per stage.
+// Pipeline (checked loop, run): the registers hold stage t+1 while stage t is
+// multiplied; halfway through stage t's MFMAs they are decoded into the other
+// LDS buffer and the loads of stage t+2 are issued, so a global load has a
+// whole stage of matrix work to arrive.  One barrier per stage.  Full tiles
+// of the multi-column tile shapes run run_pipe instead: two raw register
+// sets, each stage's decode spread over its MFMA steps.
 // b may also have its K dim contiguous (the transposed gradient view of the
-// matmul backward); that loader transposes into the same LDS tile.
+// matmul backward); that loader transposes into the same LDS tile, which is
+// stored with a column swizzle (b_swizzle).
 // MFMA operand roles: A operand (rows) = b values -> dst rows i1;
 // B operand (columns) = a values -> dst columns i0, so the lanes of one
 // accumulator row write consecutive floats of a dst row.
@@ -43,9 +46,9 @@ namespace tiled {
 // Each loader moves a BK x BW tile (BW columns of BK consecutive K rows) of
 // one operand: load() issues the global reads of a stage into registers,
 // store() converts them to fp32 and writes the LDS tile [k][column].
-// Work is split into groups (4 floats, or 8 quantized values); thread tid
-// takes groups tid, tid+T, ...; the last round is guarded when T does not
-// divide the group count.
+// Work is split into groups (4 floats, or 8 or 16 quantized values); thread
+// tid takes groups tid, tid+T, ...; the last round is guarded when T does not
+// divide the group count (or, with REDO, repeats a group: group_index).
 
 // f(integral_constant<int, 0>()), ..., f(integral_constant<int, N-1>()):
 // a loop whose index is a compile-time constant in the body.
