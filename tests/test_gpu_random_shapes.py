@@ -1,10 +1,13 @@
-"""Parity on small random shapes: for every a type, seeded random cases with
+"""Parity on random shapes: for every a type, seeded random cases with
 any a width (f32/f16/bf16 1-40, block types 1-3 whole blocks), b widths 1-40,
 K 1-300, slice broadcast factors 1-4 (dim 2) and 1-2 (dim 3) over 1-2 a
-slices per dim, row-major or K-contiguous b, automatic kernel choice.  Each
-case is checked element by element against the oracle with the parity gate.
-The case list is drawn once from a fixed seed, so every run sees the same
-cases and a failure names its case."""
+slices per dim, row-major or K-contiguous b, automatic kernel choice; and
+medium cases (a 128-704 wide, b 64-600 wide, K up to 1024 and mostly a
+whole number of 32-row stages) whose automatic plans run the tiled kernel's
+full tiles, its pipelined loop and split K.  Each case is checked element by
+element against the oracle with the parity gate.  The case lists are drawn
+once from fixed seeds, so every run sees the same cases and a failure names
+its case."""
 import numpy as np
 import pytest
 import torch
@@ -42,6 +45,34 @@ def _cases():
 CASES = _cases()
 
 
+def _medium_cases():
+    rng = np.random.default_rng(20261203)
+    out = []
+    for a_type in TYPES:
+        qk = synth.BLOCK_VALUES[a_type]
+        for _ in range(3):
+            if qk == 1:
+                ne00 = int(rng.integers(128, 705))
+                if rng.integers(0, 2):
+                    ne00 -= ne00 % 4  # 16-byte rows: the full-tile path
+            else:
+                ne00 = qk * int(rng.integers(max(1, 128 // qk), 704 // qk + 1))
+            ne10 = int(rng.integers(64, 601))
+            if rng.integers(0, 4):
+                K = 32 * int(rng.integers(1, 33))  # whole stages
+            else:
+                K = int(rng.integers(1, 1025))
+            ne02 = 1
+            d2 = int(rng.integers(1, 3))
+            kt = bool(rng.integers(0, 2))
+            seed = int(rng.integers(0, 2 ** 31 - 1))
+            out.append((a_type, (ne00, K, ne02, 1), (ne10, K, ne02 * d2, 1), kt, seed))
+    return out
+
+
+MEDIUM_CASES = _medium_cases()
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
@@ -62,3 +93,9 @@ def test_random_small_shape(case):
     res = oracle.check(gpu, ref, den, TOL)
     assert res["ok"], (case, res)
     assert np.isfinite(gpu).all()
+
+
+@pytest.mark.parametrize("case", MEDIUM_CASES, ids=lambda c: "%s-%s-%s-%s" % (
+    synth.TYPE_NAMES[c[0]], "x".join(map(str, c[1])), "x".join(map(str, c[2])), "kt" if c[3] else "rows"))
+def test_random_medium_shape(case):
+    test_random_small_shape(case)
