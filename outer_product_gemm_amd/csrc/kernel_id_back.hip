@@ -192,18 +192,26 @@ double expected_tiles_per_expert(const IdProblem &p, int bn) {
 }
 
 // Grouped-kernel configurations the automatic choice considers: 64 x 64,
-// 128 x 80 and 128 x 128 tiles (the others can be forced).
-constexpr int kIdAuto[] = {4, 12, 0};
+// 128 x 80 and 128 x 128 tiles (the others can be forced), with their rates
+// in the grouped kernel (TileCfg::eff's unit).  The rates come from
+// graph-timed launches of each configuration, forced, on 64 q4_K experts, 8
+// of 64 routed, 512 tokens (ne00 2560 x K 1024: 323 / 334 / 403 us for
+// 64 x 64 / 128 x 80 / 128 x 128; ne00 1024 x K 2560: 357 / 407 / 439 us),
+// divided into the work the cost model below counts for each; partly filled
+// tiles and the gathered slot columns make the wider slot tiles relatively
+// slower here than in a dense OUT_PROD.
+struct IdAutoCfg {
+    int cfg;
+    double eff;
+};
+constexpr IdAutoCfg kIdAuto[] = {{4, 10.6}, {12, 8.35}, {0, 11.45}};
 
 // l->variant on entry: forced configuration + 1 (an index into kCfgs that is
 // built for the grouped kernel), or 0 for automatic.  The automatic choice
-// minimizes the estimated time: workgroups x tile area x K / eff (eff as
-// for OUT_PROD), slowed in proportion when there are fewer than 640
-// workgroups (2.5 per CU: the CUs' MFMA pipes are not kept busy), with the
-// workgroup count from the expected tiles per expert.  Measured on MI355X
-// with 64 q4_K experts, 8 of 64 routed, 512 tokens: ne00 2560 x K 1024 runs
-// best with 128 x 80 tiles (1280 workgroups), ne00 1024 x K 2560 with 64 x 64
-// (1376 workgroups; 128 x 80 leaves only 512).
+// minimizes the estimated time: workgroups x tile area x K / eff, slowed in
+// proportion when there are fewer than 640 workgroups (2.5 per CU: the CUs'
+// MFMA pipes are not kept busy), with the workgroup count from the expected
+// tiles per expert.  Both shapes above run best with 64 x 64 tiles.
 bool plan_id_back(IdProblem &p, Launch *l) {
     using namespace tiled;
     int best = -1;
@@ -213,14 +221,14 @@ bool plan_id_back(IdProblem &p, Launch *l) {
         if (best < 0) return false;
     } else {
         double best_cost = 0;
-        for (int cfg : kIdAuto) {
-            const TileCfg &c = kCfgs[cfg];
+        for (const IdAutoCfg &a : kIdAuto) {
+            const TileCfg &c = kCfgs[a.cfg];
             const double wgs = (double)((p.M + c.bm() - 1) / c.bm()) * (double)p.n_expert *
                                expected_tiles_per_expert(p, c.bn());
             const double fill = std::min(1.0, wgs / 640.0);
-            const double cost = wgs * c.bm() * c.bn() * (double)p.K / c.eff / fill;
+            const double cost = wgs * c.bm() * c.bn() * (double)p.K / a.eff / fill;
             if (best < 0 || cost < best_cost) {
-                best = cfg;
+                best = a.cfg;
                 best_cost = cost;
             }
         }
