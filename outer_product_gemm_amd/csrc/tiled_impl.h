@@ -552,6 +552,18 @@ struct BlockLoader {
     }
 };
 
+// Loaders whose decode chunks go on the first MFMA steps of a stage in the
+// pipelined loop, so the next stage's loads are issued early: the 2-byte
+// aligned K-quant blocks (q3_K, q6_K), which fetch a group with 10-11 16-bit
+// loads (m5120 k17408: q6_K 1587 -> 1536 us, q3_K 1616 -> 1578 us; the other
+// types ran as fast or slower that way, q8_0 439 -> 467 us at k5120).
+template <class L>
+struct early_chunks : std::false_type {};
+template <int BM, int BK, int T>
+struct early_chunks<BlockLoader<FmtQ3_K, BM, BK, T>> : std::true_type {};
+template <int BM, int BK, int T>
+struct early_chunks<BlockLoader<FmtQ6_K, BM, BK, T>> : std::true_type {};
+
 // a's loader for a type.  WIDE: the tile runs the pipelined full-tile loop,
 // where q4_K decodes groups of 16 values (one scale/min decode per 16); the
 // checked loop keeps groups of 8, whose tail round is spread more evenly
@@ -783,10 +795,11 @@ struct TileCore {
                         for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
                 };
                 // chunk c of the decode work (a group c < kPer, then the b
-                // tile, then the loads) runs in step c * S / (kPer + 2)
+                // tile, then the loads) runs in step c * S / (kPer + 2), or
+                // in step c for the formats with early_chunks
                 constexpr int NC = LA::kPer + 2;
-                constexpr int c = (st * NC + S - 1) / S;  // first chunk at or after this step
-                constexpr bool here = DEC && c < NC && c * S / NC == st;
+                constexpr int c = early_chunks<LA>::value ? st : (st * NC + S - 1) / S;
+                constexpr bool here = DEC && c < NC && (early_chunks<LA>::value || c * S / NC == st);
                 if constexpr (here && c == LA::kPer - 1 && kTailWave) {
                     // the last a round has groups only in the first waves:
                     // a wave-uniform branch, MFMAs on both sides
