@@ -81,7 +81,7 @@ __device__ __forceinline__ int group_index(int g) {
 // of 16-column blocks within each 64-column group.  The transposing loaders
 // then write 4 consecutive k of 16 columns into 64 different banks, and the
 // MFMA operand reads (16 or 32 consecutive columns of rows that share k / 4)
-// stay contiguous.  Narrower tiles (80 rows) are stored unswizzled.
+// stay contiguous.  Tiles 80 wide are stored unswizzled.
 template <int BW>
 __device__ __forceinline__ constexpr int b_swizzle(int k) {
     return BW % 64 == 0 ? ((k >> 2) & 3) << 4 : 0;
