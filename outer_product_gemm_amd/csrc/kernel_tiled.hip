@@ -17,13 +17,27 @@ constexpr double kEffPerUs = 17.7e3;
 constexpr double kSplitLaunchUs = 3.0;
 constexpr double kSplitBytesPerUs = 4.0e6;
 
+// A configuration's rate for a type.  The 80 x 256 tile (configuration 14)
+// decodes half as much of a per flop as 160 x 128 and stages twice as much
+// of b: measured faster for the K-quants with sub-block scales (m5120 k17408
+// n1024: q3_K 1576 -> 1551 us, q4_K 1486 -> 1470, q5_K 1501 -> 1482, q6_K
+// 1529 -> 1501), slower where the decode is cheap (f32 1359 -> 1437, f16
+// 1384 -> 1429, bf16 1371 -> 1428) and about even for the other types.
+double cfg_eff(int cfg, int a_type) {
+    const bool sub_scaled_k = a_type == OUTPROD_TYPE_Q3_K || a_type == OUTPROD_TYPE_Q4_K ||
+                              a_type == OUTPROD_TYPE_Q5_K || a_type == OUTPROD_TYPE_Q6_K;
+    if (cfg == 14 && !sub_scaled_k) return 11.9;
+    return kCfgs[cfg].eff;
+}
+
 // Estimated time (us) of a configuration with `splits` K ranges: the
 // busiest CU runs ceil(tiles * splits / 256) tiles of ksplit rows each at
 // the configuration's efficiency, plus the split's reduction.
-double cfg_cost(const TileCfg &c, const Problem &p, int splits, int64_t ksplit) {
+double cfg_cost(int cfg, const Problem &p, int splits, int64_t ksplit) {
+    const TileCfg &c = kCfgs[cfg];
     const int64_t tiles = ((p.M + c.bm() - 1) / c.bm()) * ((p.N + c.bn() - 1) / c.bn()) * p.ne12 * p.ne13;
     const int64_t per_cu = (tiles * splits + 255) / 256;
-    double t = (double)per_cu * c.bm() * c.bn() * (double)ksplit / c.eff / kEffPerUs;
+    double t = (double)per_cu * c.bm() * c.bn() * (double)ksplit / cfg_eff(cfg, p.a_type) / kEffPerUs;
     if (splits > 1)
         t += kSplitLaunchUs + (double)(2 * splits) * p.M * p.N * p.ne12 * p.ne13 * 4 / kSplitBytesPerUs;
     return t;
@@ -62,7 +76,7 @@ bool plan_tiled(const Problem &p, Launch *l) {
     for (int i = c_lo; i <= c_hi; ++i) {
         for (int sp = s_lo; sp <= s_hi; ++sp) {
             const int64_t ks = forced_splits > 0 ? (p.K + sp - 1) / sp : split_rows(p.K, sp);
-            const double c = cfg_cost(kCfgs[i], p, sp, ks);
+            const double c = cfg_cost(i, p, sp, ks);
             if (first || c < best_cost) {
                 best = i;
                 best_splits = sp;

@@ -898,10 +898,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     const int K = (int)p.K, M = (int)p.M, N = (int)p.N;
 
     // the pipelined loop needs registers for two raw stages next to the
-    // accumulators (not the column-of-waves tiles: with 17 accumulator blocks
-    // per wave they spill) and a step per a group plus two
-    constexpr bool kPipeCfg = WGM > 1;
-    typename ALoaderFor<AT, BM, BK, T, kPipeCfg>::type la;
+    // accumulators (not the column-of-waves tiles: with 68 accumulator
+    // registers per wave they spill) and a step per a group plus two; q4_K
+    // takes 16-value groups there when their last round fills whole waves
+    constexpr bool kPipeCfg = FM * FN * C::MM::NR <= 64;
+    constexpr int kG16 = BK * BM / 16;
+    constexpr bool kWide = kPipeCfg && (kG16 % T == 0 || kG16 % T % 64 == 0);
+    typename ALoaderFor<AT, BM, BK, T, kWide>::type la;
     typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T, true>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
@@ -1044,6 +1047,9 @@ struct TileCfg {
 // 11: as 4 with 32-row stages
 // 12: 128 x 80, 4 waves of 32 x 80 (16x16x4) -- 80-slot tiles (routed experts)
 // 13: 64 x 80,  4 waves of 16 x 80 (16x16x4)
+// 14: 80 x 256, 8 waves of 80 x 32 (16x16x4) in one row, 32-row stages --
+//     m5120 x n1024 in 256 tiles with half the a decode per flop of 8 (the
+//     planner rates it per a type: cfg_eff)
 constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 16, 12.4f},
     {16, 5, 2, 2, 4, 16, 11.5f},
@@ -1059,6 +1065,7 @@ constexpr TileCfg kCfgs[] = {
     {32, 1, 1, 2, 2, 32, 10.5f},
     {16, 2, 5, 4, 1, 16, 10.4f},
     {16, 1, 5, 4, 1, 16, 10.0f},
+    {16, 5, 2, 1, 8, 32, 12.5f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -1084,6 +1091,7 @@ const void *tiled_fn(int variant) {
     case 11: return cfg_fn<AT, 11, BT>();
     case 12: return cfg_fn<AT, 12, BT>();
     case 13: return cfg_fn<AT, 13, BT>();
+    case 14: return cfg_fn<AT, 14, BT>();
     default: return cfg_fn<AT, 0, BT>();
     }
 }

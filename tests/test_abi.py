@@ -158,7 +158,7 @@ def test_forced_kernels():
         assert p["kernel_name"] == "skinny" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 11))] == "E_KERNEL"
     # every tiled configuration can be forced; an unknown one is refused
-    for cfg in range(14):
+    for cfg in range(15):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, 40))] == "E_KERNEL"

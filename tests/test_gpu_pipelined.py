@@ -25,11 +25,11 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 # stage rows (BK) of each tiled configuration, as out_prod_plan reports them
 STAGE_ROWS = {0: 16, 1: 16, 2: 16, 3: 16, 4: 16, 5: 16, 6: 16,
-              7: 32, 8: 32, 9: 32, 10: 32, 11: 32, 12: 16, 13: 16}
-# i0 = 512 (a multiple of every block size): full 128/160/256-wide tiles and
-# a ragged last one for 160 and 272; i1 = 200: full 64/80/128-row tiles and
-# a ragged last one
-M, N = 512, 200
+              7: 32, 8: 32, 9: 32, 10: 32, 11: 32, 12: 16, 13: 16, 14: 32}
+# i0 = 512 (a multiple of every block size): full 64/80/128/160/256-wide
+# tiles and a ragged last one for 80, 160 and 272; i1 = 300: full
+# 64/80/128/256-row tiles and a ragged last one
+M, N = 512, 300
 OTHER_TYPES = [synth.Q8_0, synth.F16, synth.BF16, synth.Q4_0, synth.Q4_1, synth.Q5_0,
                synth.Q5_1, synth.Q2_K, synth.Q3_K, synth.Q5_K, synth.Q6_K]
 
@@ -65,7 +65,7 @@ def _stage_rows(inst, code):
                            inst.nb, code)["tile_k"]
 
 
-@pytest.mark.parametrize("cfg", range(14))
+@pytest.mark.parametrize("cfg", range(15))
 def test_full_tiles_every_stage_count(cfg):
     code = B.kernel_code(B.KERNEL_TILED, cfg)
     bk = STAGE_ROWS[cfg]
