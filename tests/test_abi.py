@@ -144,6 +144,25 @@ def test_kernel_choice_on_workloads():
         assert p["grid"] >= 1
 
 
+def test_tile_choice_at_the_27B_shapes():
+    """The planner's measured tile choices at m5120 k17408 n1024 (one launch
+    per CU round): the 80 x 256 tile (configuration 14, half the a decode per
+    flop) for the K-quants with sub-block scales, 160 x 128 (configuration
+    8) for the types whose decode is cheap; 272 x 128 (configuration 9) for
+    m17408 k5120; the K-contiguous 27B input gradient like its type."""
+    for name, cfg in (("q4_K_5120x17408", 14), ("q6_K_5120x17408", 14), ("q3_K_5120x17408", 14),
+                      ("q5_K_5120x17408", 14), ("f32_5120x17408", 8), ("f16_5120x17408", 8),
+                      ("q8_0_5120x17408", 8), ("q4_0_5120x17408", 8), ("q4_K_17408x5120", 9),
+                      ("q8_0_5120", 8), ("lora27B_dxW", 14)):
+        inst_spec = synth.WORKLOADS[name]
+        a_type, a_ne, b_ne = inst_spec[:3]
+        kt = inst_spec[7] if len(inst_spec) > 7 else False
+        ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne, kt)
+        p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
+        assert p["kernel_name"] == "tiled" and p["variant"] == cfg and p["splits"] == 1, (name, p)
+        assert p["grid"] == (256 if cfg != 9 else 512), (name, p)
+
+
 def test_forced_kernels():
     ne, nb = base()
     assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_TILED)["kernel_name"] == "tiled"
