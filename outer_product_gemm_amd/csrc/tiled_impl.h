@@ -877,7 +877,7 @@ struct TileCore {
 
 template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int tiles_m,
-                                                               int tiles_n) {
+                                                               int tiles_n, int n_fast) {
     typedef TileCore<MF, FM, FN, WGM, WGN, BK> C;
     constexpr int T = C::T, BM = C::BM, BN = C::BN;
     __shared__ __attribute__((aligned(16))) float As[2][BK][C::LDA];
@@ -891,7 +891,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     const int slices = (int)(p0.ne12 * p0.ne13);
     const int zz = logical / per_slice, rem = logical % per_slice;
     const int z = zz % slices, sp = zz / slices;
-    const int m0 = (rem % tiles_m) * BM, n0 = (rem / tiles_m) * BN;
+    // n_fast: consecutive logical tiles walk i1 (they share a's strip)
+    // instead of i0 (sharing b's strip)
+    const int m0 = (n_fast ? rem / tiles_n : rem % tiles_m) * BM;
+    const int n0 = (n_fast ? rem % tiles_n : rem / tiles_m) * BN;
     Problem p = p0;
     SliceBase s = slice_base(p, z);
     if (p.splits > 1) apply_split(p, s, z, sp);
