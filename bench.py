@@ -64,15 +64,15 @@ PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0}
 # scaled by the copy-kernel calibration), keyed by workload, valid only for
 # the kernel sources whose hash is recorded with it.
 MEASURED_TRAFFIC = {
-    # profiles/tiled_q4K_27B_lora_backward.md: launch A 378.6 MB, launch B 523.3 MB
-    "q4_K_27B_both": {"kernel_hash": "4a5c2c512b0230ac", "bytes_per_launch": 450.92e6},
+    # profiles/tiled_q4K_27B_lora_backward.md: launch A 378.3 MB, launch B 472.2 MB
+    "q4_K_27B_both": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 425.25e6},
     # profiles/lora_linear_backward_4B_27B.md: the tiled launches (split dx_W main kernel
     # and dx_A); the split's reduce kernel is reported there separately
-    "lora_4B_linear_backward": {"kernel_hash": "4a5c2c512b0230ac", "bytes_per_launch": 37.31e6},
+    "lora_4B_linear_backward": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 37.01e6},
     # profiles/column_lora_rank_and_deltanet.md
-    "lora_r8_9216": {"kernel_hash": "4a5c2c512b0230ac", "bytes_per_launch": 19.40e6},
+    "lora_r8_9216": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 19.40e6},
     # profiles/id_back_moe_q4_K.md: the grouped tiled launches (routing kernels separate)
-    "moe_back_q4_K": {"kernel_hash": "4a5c2c512b0230ac", "bytes_per_launch": 172.64e6},
+    "moe_back_q4_K": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 172.65e6},
 }
 
 
