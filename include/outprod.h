@@ -41,29 +41,36 @@
  * The library keeps no pointer to them after a call returns.  A call only
  * enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
  * returns; the buffers must stay alive until the stream has passed it.
- * dst is overwritten (not accumulated into).  Results are deterministic:
- * every dst element has one writer and a fixed summation order, also when K
- * is split (see below).
+ * dst is overwritten (not accumulated into).
  *
  * Split K and the workspace: when a problem has too few output tiles to fill
  * the GPU but a long K, the library splits K into ranges (outprod_plan.splits)
  * that run in parallel and write partial results to a workspace; a second
- * kernel on the same stream adds the partials in range order into dst.  The
- * workspace (64 MiB) belongs to the library, one per (device, stream) pair,
- * allocated with hipMalloc by the first call on that stream whose plan splits
- * K and kept until the process ends (never freed, so a captured graph that
- * uses it stays valid).  Consequences:
+ * kernel on the same stream adds the partials in range order into dst.
+ * MUL_MAT_ID_BACK keeps its routing tables in a workspace too.  Workspaces
+ * (64 MiB each) belong to the library, at most 4 per device, each bound to
+ * one stream, so the library holds at most 256 MiB per device:
+ *   - A stream's first call that needs a workspace allocates one (hipMalloc)
+ *     and binds it to the stream.  It stays bound until
+ *     out_prod_release_stream frees it, so a graph captured on the stream
+ *     keeps a valid address.
  *   - Calls on one stream are ordered by the stream; calls on different
  *     streams use different workspaces and may overlap.  A HIP graph keeps
  *     using the workspace of the stream it was captured on: do not replay it
  *     concurrently with calls on that stream or with another replay of a
- *     graph captured there.
- *   - The allocation cannot happen while the stream is being captured: a
- *     splitting call on a capturing stream that has no workspace yet returns
- *     OUTPROD_E_CAPTURE without enqueuing anything.  One uncaptured call on
- *     that stream beforehand (any splitting problem) avoids it.
- * The library's only mutable state is that table, guarded by a mutex; calls
- * may come from any thread.
+ *     graph captured there, and do not release that stream while the graph
+ *     may still be replayed.
+ *   - When a splitting out_prod finds no workspace for its stream (4 are
+ *     bound to other streams, or the stream is capturing and has none), it
+ *     runs the unsplit plan instead: the same sum in another order, slower
+ *     for these shapes, within the same accuracy.  A forced split
+ *     (out_prod_ex) returns OUTPROD_E_WORKSPACE or OUTPROD_E_CAPTURE instead,
+ *     and so does out_prod_id_back, which has no workspace-free plan.
+ * Results are deterministic for a given plan: every dst element has one
+ * writer and a fixed summation order, also when K is split.  The plan
+ * depends on the problem only, except for the fallback just described.
+ * The library's only mutable state is the pool's table, guarded by a mutex;
+ * calls may come from any thread.
  *
  * Errors: every function returns OUTPROD_OK (0) or a negative status.  All
  * argument checks happen on the host before any HIP call, and on error dst
@@ -121,8 +128,11 @@ extern "C" {
 #define OUTPROD_E_KERNEL (-11)   /* a forced kernel that cannot run this problem */
 #define OUTPROD_E_HIP (-12)      /* a HIP call failed: kernel launch (e.g. no gfx950
                                     device) or the workspace allocation */
-#define OUTPROD_E_CAPTURE (-13)  /* the plan splits K, the stream is capturing a graph and
-                                    has no workspace yet (see "Split K" above) */
+#define OUTPROD_E_CAPTURE (-13)  /* the call needs a workspace and the stream is capturing
+                                    a graph and has none (see "Split K" above); or a
+                                    release under capture */
+#define OUTPROD_E_WORKSPACE (-14) /* the call needs a workspace and the device's 4 are
+                                     bound to other streams */
 
 /*
  * out_prod: dst = OUT_PROD(a, b) as defined above, enqueued on `stream`.
@@ -167,6 +177,9 @@ typedef struct outprod_plan {
     int64_t ksplit;   /* K rows per range (the last range may be shorter) */
     int64_t workspace_bytes; /* partial results: splits * ne00 * ne10 * slices * 4
                                 (0 without a split); at most 64 MiB */
+    int tile_order;   /* tiled kernel: 0 = consecutive workgroups walk i0 fastest
+                         within a slice, 1 = i1 fastest; -1 for other kernels */
+    int reserved;     /* 0 */
 } outprod_plan;
 
 /*
@@ -188,10 +201,13 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
  * outprod_plan.variant; 0 lets the library choose.  Bits 16-23 may force
  * the split count of K (with a forced family only): 1 = no split, n = n
  * ranges of ceil(K/n) rows (fewer when K is short); 0 lets the library
- * choose.  A family, configuration or split that cannot run the problem
- * returns OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a, an unknown
- * configuration index, more ranges than K rows or partials beyond the
- * workspace).
+ * choose.  Bits 24-30 may force the tiled kernel's tile order (with the
+ * TILED family only): (order + 1) << 24 with the order as reported in
+ * outprod_plan.tile_order; 0 lets the library choose.  A family,
+ * configuration, split or order that cannot run the problem returns
+ * OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a, an unknown configuration
+ * index, more ranges than K rows, partials beyond the workspace, an order
+ * with another family).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);
@@ -219,7 +235,8 @@ int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
  *
  * The slots are grouped by expert on the device (three small routing kernels,
  * tables in the stream's workspace -- see "Split K and the workspace" above,
- * including OUTPROD_E_CAPTURE), then one tiled launch runs every expert's
+ * including OUTPROD_E_CAPTURE and OUTPROD_E_WORKSPACE), then one tiled launch
+ * runs every expert's
  * slots; 4 launches on `stream`.  A slot whose id is outside [0, n_expert) gets
  * a row of NaN (ids are device data; there is no host-side check).  K == 0
  * writes zeros without reading ids; no slots or ne00 == 0: no work.
@@ -242,10 +259,31 @@ int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int
                           const float *dst, const int64_t ne[16], const int64_t nb[16], int kernel,
                           outprod_plan *plan);
 
+/*
+ * out_prod_release_stream: free the workspace bound to `stream` (a
+ * hipStream_t; NULL = the current device's default stream), if any, after
+ * waiting for the work queued on `stream` (hipStreamSynchronize).  Call it
+ * before destroying a stream that made splitting or MUL_MAT_ID_BACK calls,
+ * and only when no graph captured on that stream will be replayed again.
+ * It frees device memory, so it must not run while any thread of the process
+ * is capturing a graph in global capture mode.  Returns OUTPROD_OK (also
+ * when nothing is bound), OUTPROD_E_CAPTURE if `stream` is capturing, or
+ * OUTPROD_E_HIP.
+ */
+int out_prod_release_stream(void *stream);
+
+/*
+ * out_prod_workspace_count: how many workspaces the library holds on the
+ * current device (at most 4).  OUTPROD_E_NULL for a NULL argument,
+ * OUTPROD_E_HIP without a device.
+ */
+int out_prod_workspace_count(int *count);
+
 /* A static English description of a status code; never NULL. */
 const char *out_prod_strerror(int status);
 
-/* Library ABI version: 2 (1 had no split fields in outprod_plan). */
+/* Library ABI version: 3 (2 had no tile_order in outprod_plan and no
+ * workspace pool calls; 1 had no split fields). */
 int out_prod_version(void);
 
 #ifdef __cplusplus

@@ -37,26 +37,29 @@ OUTPROD_OK = 0
 STATUS = {
     -1: "E_NULL", -2: "E_TYPE", -3: "E_SHAPE", -4: "E_K", -5: "E_DST_SHAPE", -6: "E_BCAST",
     -7: "E_QK", -8: "E_LAYOUT", -9: "E_ALIAS", -10: "E_RANGE", -11: "E_KERNEL", -12: "E_HIP",
-    -13: "E_CAPTURE",
+    -13: "E_CAPTURE", -14: "E_WORKSPACE",
 }
 KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
 
 
-def kernel_code(family: int, config: int = None, splits: int = None) -> int:
+def kernel_code(family: int, config: int = None, splits: int = None, order: int = None) -> int:
     """out_prod_ex's kernel argument: a family, optionally with a forced
-    configuration index (as reported by out_prod_plan's ``variant``) and a
-    forced split count of K (1 = no split)."""
+    configuration index (as reported by out_prod_plan's ``variant``), a
+    forced split count of K (1 = no split) and a forced tile order of the
+    tiled kernel (as reported by out_prod_plan's ``tile_order``)."""
     code = family | ((config + 1) << 8 if config is not None else 0)
-    return code | (splits << 16 if splits is not None else 0)
+    code |= splits << 16 if splits is not None else 0
+    return code | ((order + 1) << 24 if order is not None else 0)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
 # The library ABI this binding's structures and signatures match.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol the header declares.
 EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_id_back", "out_prod_id_back_ex",
-           "out_prod_id_back_plan", "out_prod_strerror", "out_prod_version")
+           "out_prod_id_back_plan", "out_prod_release_stream", "out_prod_workspace_count",
+           "out_prod_strerror", "out_prod_version")
 _I64x16 = ctypes.c_int64 * 16
 
 
@@ -72,7 +75,8 @@ class outprod_plan(ctypes.Structure):
                 ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
                 ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int),
                 ("swapped", ctypes.c_int), ("splits", ctypes.c_int), ("ksplit", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("tile_order", ctypes.c_int),
+                ("reserved", ctypes.c_int)]
 
 
 _I64x12 = ctypes.c_int64 * 12
@@ -107,6 +111,10 @@ def load_library(path: str = LIB_PATH):
             lib.out_prod_id_back_plan.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64p, i64p,
                                                   ctypes.c_int, ctypes.POINTER(outprod_plan)]
             lib.out_prod_id_back_plan.restype = ctypes.c_int
+            lib.out_prod_release_stream.argtypes = [vp]
+            lib.out_prod_release_stream.restype = ctypes.c_int
+            lib.out_prod_workspace_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
+            lib.out_prod_workspace_count.restype = ctypes.c_int
             lib.out_prod_strerror.argtypes = [ctypes.c_int]
             lib.out_prod_strerror.restype = ctypes.c_char_p
             lib.out_prod_version.restype = ctypes.c_int
@@ -135,6 +143,19 @@ def _arr16(x):
 def _check(status: int) -> None:
     if status != OUTPROD_OK:
         raise OutProdError(status, out_prod_strerror(status))
+
+
+def out_prod_release_stream(stream: int = 0) -> None:
+    """C ``out_prod_release_stream``: wait for ``stream`` and free the
+    workspace the library holds for it."""
+    _check(load_library().out_prod_release_stream(stream or None))
+
+
+def out_prod_workspace_count() -> int:
+    """C ``out_prod_workspace_count``: workspaces held on the current device."""
+    n = ctypes.c_int(0)
+    _check(load_library().out_prod_workspace_count(ctypes.byref(n)))
+    return n.value
 
 
 def out_prod_strerror(status: int) -> str:
@@ -221,32 +242,48 @@ def plan_status(a: int, a_type: int, b: int, dst: int, ne, nb, kernel: int = KER
 
 # ---------------------------------------------------------------- torch tensors
 
+# dtypes an f32 / f16 / bf16 ``a`` may have (2-byte integer tensors may hold
+# the bits of the half types); block-quantized ``a`` is uint8
+_A_DTYPES = {F32: (torch.float32,), F16: (torch.float16, torch.int16),
+             BF16: (torch.bfloat16, torch.int16)}
+
+
 def tensor_ne_nb(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tensor, a_ne0=None):
     """ggml ne/nb of torch tensors laid out (ne3, ne2, ne1, ne0) (fewer dims are
     padded with leading 1s).  An f32 / f16 / bf16 ``a`` is a tensor of that
     dtype (or of 2-byte integers holding the bits); a block-quantized ``a`` is
     a uint8 tensor whose last dim is the row's bytes; ``a_ne0`` gives its
-    value count."""
+    value count.  b and out must be float32.  Raises ValueError for any other
+    dtype (byte strides are the element strides times the element size, so
+    a wrong dtype would describe memory the tensor does not own)."""
+    if a_type not in BLOCK_VALUES:
+        raise ValueError("unknown a_type %r" % (a_type,))
+    want = _A_DTYPES.get(a_type, (torch.uint8,))
+    if a.dtype not in want:
+        raise ValueError("a has dtype %s; a_type %d needs %s" % (a.dtype, a_type, " or ".join(map(str, want))))
+    if b.dtype != torch.float32:
+        raise ValueError("b must be float32, not %s" % b.dtype)
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32, not %s" % out.dtype)
+    for name, t in (("a", a), ("b", b), ("out", out)):
+        if t.dim() > 4:
+            raise ValueError("%s has %d dims; at most 4" % (name, t.dim()))
+
     def four(t):
         shape = [1] * (4 - t.dim()) + list(t.shape)
         stride = [0] * (4 - t.dim()) + list(t.stride())
-        return shape[::-1], stride[::-1]
+        return shape[::-1], [t.element_size() * x for x in stride[::-1]]
     ash, ast = four(a)
     bsh, bst = four(b)
     osh, ost = four(out)
     if BLOCK_VALUES[a_type] == 1:
-        a_ne = ash
-        a_nb = [a.element_size() * s for s in ast]
-        if a.element_size() != BLOCK_BYTES[a_type]:
-            raise ValueError("a's element size %d does not match the type" % a.element_size())
+        a_ne, a_nb = ash, ast
     else:
         if a_ne0 is None:
             a_ne0 = ash[0] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]
         a_ne = [a_ne0] + ash[1:]
         a_nb = [BLOCK_BYTES[a_type]] + list(ast[1:])
-    ne = a_ne + bsh + osh
-    nb = a_nb + [4 * s for s in bst] + [4 * s for s in ost]
-    return ne, nb
+    return a_ne + bsh + osh, a_nb + bst + ost
 
 
 def out_prod_tensors(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.Tensor = None,
@@ -256,14 +293,22 @@ def out_prod_tensors(a: torch.Tensor, a_type: int, b: torch.Tensor, out: torch.T
     a: f32 / f16 / bf16 (ne03, ne02, K, ne00), or uint8 (ne03, ne02, K, row_bytes)
        for the block types;
     b: f32 (ne13, ne12, K, ne10); out: f32 (ne13, ne12, ne10, ne00), allocated if None.
+    All three must be on the same GPU (ValueError otherwise, before any launch).
     """
+    if b.device.type != "cuda":
+        raise ValueError("b must be a GPU tensor, not on %s" % b.device)
     if out is None:
         bsh = [1] * (4 - b.dim()) + list(b.shape)
-        if BLOCK_VALUES[a_type] == 1:
+        if BLOCK_VALUES.get(a_type) == 1:
             ne00 = a.shape[-1]
-        else:
+        elif a_type in BLOCK_VALUES:
             ne00 = a_ne0 if a_ne0 is not None else a.shape[-1] // BLOCK_BYTES[a_type] * BLOCK_VALUES[a_type]
+        else:
+            raise ValueError("unknown a_type %r" % (a_type,))
         out = torch.empty((bsh[0], bsh[1], bsh[3], ne00), dtype=torch.float32, device=b.device)
+    for name, t in (("a", a), ("out", out)):
+        if t.device != b.device:
+            raise ValueError("%s is on %s, b on %s: all tensors must be on one GPU" % (name, t.device, b.device))
     ne, nb = tensor_ne_nb(a, a_type, b, out, a_ne0)
     if stream is None:
         stream = torch.cuda.current_stream(b.device)

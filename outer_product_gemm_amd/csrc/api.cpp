@@ -110,8 +110,11 @@ Problem swap_operands(const Problem &p) {
     return q;
 }
 
+// no_split: plan without a K split unless one is forced (for a call that
+// has no workspace).
 int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
-                      const int64_t *ne, const int64_t *nb, int kernel, Checked *c) {
+                      const int64_t *ne, const int64_t *nb, int kernel, Checked *c,
+                      bool no_split = false) {
     if (!ne || !nb) return OUTPROD_E_NULL;
     if (block_bytes(a_type) == 0) return OUTPROD_E_TYPE;
     for (int i = 0; i < 12; ++i)
@@ -232,17 +235,21 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
         return l.grid > lim ? OUTPROD_E_RANGE : OUTPROD_OK;
     }
 
-    // kernel = family | (tile configuration + 1) << 8 | splits << 16;
-    // configuration 0 and splits 0 = automatic
+    // kernel = family | (tile configuration + 1) << 8 | splits << 16 |
+    // (tile order + 1) << 24; configuration 0, splits 0 and order 0 =
+    // automatic
     const int variant = (kernel >> 8) & 0xFF;
     const int splits = (kernel >> 16) & 0xFF;
-    if (kernel >> 24) return OUTPROD_E_KERNEL;
+    const int order = (kernel >> 24) & 0x7F;
+    if (order > 2) return OUTPROD_E_KERNEL;
     kernel &= 0xFF;
     if ((variant != 0 || splits != 0) && kernel != OUTPROD_KERNEL_TILED &&
         kernel != OUTPROD_KERNEL_SKINNY)
         return OUTPROD_E_KERNEL;
+    if (order != 0 && kernel != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
+    l.order = order - 1;
     l.variant = variant;
-    l.splits = splits;
+    l.splits = splits == 0 && no_split ? 1 : splits;
     bool ok;
     switch (kernel) {
     case OUTPROD_KERNEL_AUTO: {
@@ -282,8 +289,13 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     return OUTPROD_OK;
 }
 
-// The split-K workspaces: one per (device, stream), allocated on first use
-// and never freed (graphs captured on the stream keep their address).
+// The library's workspaces (split-K partials, MUL_MAT_ID_BACK routing
+// tables): at most kMaxWorkspaces per device, kWorkspaceBytes each, each
+// bound to one stream.  A stream's first call that needs one allocates it
+// (never under capture), and it stays bound -- a graph captured on the stream
+// keeps its address -- until out_prod_release_stream frees it.  So the
+// library holds at most kMaxWorkspaces * kWorkspaceBytes per device however
+// many streams come and go.
 struct Workspace {
     int device;
     hipStream_t stream;
@@ -292,16 +304,24 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
 
+// The workspace of `stream` on the current device, allocated on its first
+// use.  OUTPROD_E_WORKSPACE: the device already has kMaxWorkspaces, bound to
+// other streams; OUTPROD_E_CAPTURE: the stream has none and is capturing (an
+// allocation would invalidate the capture).
 int stream_workspace(hipStream_t stream, uint8_t **out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return OUTPROD_E_HIP;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int on_dev = 0;
     for (const Workspace &w : g_ws) {
-        if (w.device == dev && w.stream == stream) {
+        if (w.device != dev) continue;
+        ++on_dev;
+        if (w.stream == stream) {
             *out = w.ptr;
             return OUTPROD_OK;
         }
     }
+    if (on_dev >= kMaxWorkspaces) return OUTPROD_E_WORKSPACE;
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &st) != hipSuccess) return OUTPROD_E_HIP;
     if (st != hipStreamCaptureStatusNone) return OUTPROD_E_CAPTURE;
@@ -309,6 +329,29 @@ int stream_workspace(hipStream_t stream, uint8_t **out) {
     if (hipMalloc(&ptr, (size_t)kWorkspaceBytes) != hipSuccess) return OUTPROD_E_HIP;
     g_ws.push_back(Workspace{dev, stream, (uint8_t *)ptr});
     *out = (uint8_t *)ptr;
+    return OUTPROD_OK;
+}
+
+// Free the workspace of `stream` (for the NULL stream: the current
+// device's) once the stream's queued work has finished with it.
+int release_stream(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return OUTPROD_E_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    size_t i = 0;
+    while (i < g_ws.size() && !(g_ws[i].stream == stream && (stream != nullptr || g_ws[i].device == dev)))
+        ++i;
+    if (i == g_ws.size()) return OUTPROD_OK;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return OUTPROD_E_HIP;
+    if (st != hipStreamCaptureStatusNone) return OUTPROD_E_CAPTURE;
+    const Workspace w = g_ws[i];
+    if (w.device != dev && hipSetDevice(w.device) != hipSuccess) return OUTPROD_E_HIP;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipFree(w.ptr);
+    if (w.device != dev) (void)hipSetDevice(dev);
+    if (e != hipSuccess) return OUTPROD_E_HIP;
+    g_ws.erase(g_ws.begin() + (std::ptrdiff_t)i);
     return OUTPROD_OK;
 }
 
@@ -321,10 +364,19 @@ int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne
     if (c.l.splits > 1) {
         uint8_t *ws = nullptr;
         rc = stream_workspace(s, &ws);
-        if (rc != OUTPROD_OK) return rc;
-        c.p.splits = c.l.splits;
-        c.p.ksplit = c.l.ksplit;
-        c.p.ws = ws;
+        if (rc == OUTPROD_E_CAPTURE || rc == OUTPROD_E_WORKSPACE) {
+            // no workspace for this stream: an automatic plan runs unsplit
+            // instead (the same sum in another order; a forced split fails)
+            if ((kernel >> 16) & 0xFF) return rc;
+            rc = validate_and_plan(a, a_type, b, dst, ne, nb, kernel, &c, true);
+            if (rc != OUTPROD_OK) return rc;
+        } else if (rc != OUTPROD_OK) {
+            return rc;
+        } else {
+            c.p.splits = c.l.splits;
+            c.p.ksplit = c.l.ksplit;
+            c.p.ws = ws;
+        }
     }
     hipError_t e = hipSuccess;
     switch (c.l.kernel) {
@@ -532,6 +584,7 @@ int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int
     plan->splits = 1;
     plan->ksplit = c.p.K;
     plan->workspace_bytes = c.l.kernel == OUTPROD_KERNEL_TILED ? outprod::id_workspace_bytes(c.p) : 0;
+    plan->tile_order = -1;
     return OUTPROD_OK;
 }
 
@@ -569,6 +622,22 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
     plan->splits = c.l.splits > 1 ? c.l.splits : 1;
     plan->ksplit = c.l.splits > 1 ? c.l.ksplit : c.p.K;
     plan->workspace_bytes = outprod::split_bytes(c.p, plan->splits);
+    plan->tile_order = c.l.kernel == OUTPROD_KERNEL_TILED ? c.l.order : -1;
+    return OUTPROD_OK;
+}
+
+int out_prod_release_stream(void *stream) {
+    return outprod::release_stream((hipStream_t)stream);
+}
+
+int out_prod_workspace_count(int *count) {
+    if (!count) return OUTPROD_E_NULL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return OUTPROD_E_HIP;
+    std::lock_guard<std::mutex> lock(outprod::g_ws_mutex);
+    *count = 0;
+    for (const outprod::Workspace &w : outprod::g_ws)
+        if (w.device == dev) ++*count;
     return OUTPROD_OK;
 }
 
@@ -588,12 +657,15 @@ const char *out_prod_strerror(int status) {
     case OUTPROD_E_KERNEL: return "the requested kernel cannot run this problem";
     case OUTPROD_E_HIP: return "a HIP call failed (kernel launch or workspace allocation)";
     case OUTPROD_E_CAPTURE:
-        return "K is split and the capturing stream has no workspace yet: make one uncaptured "
-               "call on this stream first";
+        return "the call needs a workspace, the stream is capturing a graph and has none "
+               "bound (or a release under capture): make one uncaptured call on this stream first";
+    case OUTPROD_E_WORKSPACE:
+        return "the device's workspaces (4) are all bound to other streams: release a stream "
+               "that no longer needs one with out_prod_release_stream";
     default: return "unknown status";
     }
 }
 
-int out_prod_version(void) { return 2; }
+int out_prod_version(void) { return 3; }
 
 }  // extern "C"

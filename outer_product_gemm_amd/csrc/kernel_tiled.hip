@@ -106,6 +106,7 @@ bool plan_tiled(const Problem &p, Launch *l) {
     l->splits = best_splits;
     l->ksplit = best_splits > 1 ? ksplit : p.K;
     l->grid = tm * tn * p.ne12 * p.ne13 * best_splits;
+    if (l->order < 0) l->order = tile_order_n_fast(p, *l, tm, tn);
     return true;
 }
 
@@ -132,7 +133,7 @@ int tile_order_n_fast(const Problem &p, const Launch &l, int64_t tiles_m, int64_
 hipError_t launch_tiled(const Problem &p, const Launch &l, hipStream_t s) {
     int tiles_m = (int)((p.M + l.tile_m - 1) / l.tile_m);
     int tiles_n = (int)((p.N + l.tile_n - 1) / l.tile_n);
-    int n_fast = tile_order_n_fast(p, l, tiles_m, tiles_n);
+    int n_fast = l.order;
     Problem pp = p;
     void *args[] = {&pp, &tiles_m, &tiles_n, &n_fast};
     const void *fn = nullptr;

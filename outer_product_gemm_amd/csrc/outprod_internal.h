@@ -36,8 +36,12 @@ struct Problem {
     uint8_t *ws;
 };
 
-// Bytes of the per-(device, stream) workspace; split plans never need more.
+// Bytes of one workspace of the library's pool; split plans never need more.
 constexpr int64_t kWorkspaceBytes = 64ll << 20;
+// Workspaces per device at most (each bound to one stream at a time).
+constexpr int kMaxWorkspaces = 4;
+// Bytes of the allocation-free entry point's static device scratch.
+constexpr int64_t kScratchBytes = 32ll << 20;
 
 // Workspace bytes a split plan needs (0 without a split).
 inline int64_t split_bytes(const Problem &p, int splits) {
@@ -54,6 +58,8 @@ struct Launch {
     int64_t grid;     // main kernel workgroups (all splits)
     int splits;       // 1 = no split
     int64_t ksplit;   // rows per split
+    int order;        // tiled kernel: 0 = tiles walk i0 fastest within a slice,
+                      // 1 = i1 fastest; on entry to plan_tiled, -1 = automatic
 };
 
 // One validated MUL_MAT_ID_BACK problem: for routed slot s = i + n_used*t,
@@ -88,6 +94,7 @@ hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s);
 // Per-kernel planning (host only, no HIP calls) and launching.
 bool plan_skinny(const Problem &p, Launch *l);
 bool plan_tiled(const Problem &p, Launch *l);
+int tile_order_n_fast(const Problem &p, const Launch &l, int64_t tiles_m, int64_t tiles_n);
 void plan_zero(const Problem &p, Launch *l);
 
 hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.out_prod_version() == 2
+    assert B.out_prod_version() == 3
     for code in [0] + list(B.STATUS):
         msg = B.out_prod_strerror(code)
         assert msg and msg != "unknown status"
@@ -352,3 +352,60 @@ def test_id_back_every_type_plans(a_type):
     inst_ne, inst_nb = synth.moe_ne_nb(a_type, 256 if qk > 1 else 100, 64, 4, 2, 8)
     p = B.out_prod_id_back_plan(A, a_type, G_, I_, D, inst_ne, inst_nb)
     assert p["kernel_name"] == "tiled"
+
+
+def test_tile_order_reported_and_forced():
+    """The tiled kernel's tile order within a slice (i0 or i1 fastest) is
+    reported by the plan, chosen per shape (i1 fastest for the tall m17408
+    q4_K weight, i0 fastest at m5120) and can be forced either way; other
+    families refuse an order and report -1."""
+    for name, want in (("q4_K_5120x17408", 0), ("q4_K_17408x5120", 1)):
+        a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
+        ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
+        p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
+        assert p["kernel_name"] == "tiled" and p["tile_order"] == want, (name, p)
+        for order in (0, 1):
+            code = B.kernel_code(B.KERNEL_TILED, p["variant"], None, order)
+            q = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb, code)
+            assert q["tile_order"] == order and q["variant"] == p["variant"] and q["grid"] == p["grid"]
+        bad = B.kernel_code(B.KERNEL_TILED) | (3 << 24)
+        assert B.STATUS[B.plan_status(A, a_type, 0x40000000000, 0x80000000000, ne, nb, bad)] == "E_KERNEL"
+    ne, nb = base()
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["tile_order"] == -1
+    for fam in (B.KERNEL_SKINNY, B.KERNEL_AUTO):
+        code = B.kernel_code(fam, None, None, 0)
+        assert B.STATUS[plan(synth.F32, ne, nb, kernel=code)] == "E_KERNEL"
+
+
+def test_tensor_helpers_refuse_wrong_dtypes_and_devices():
+    """out_prod_tensors / tensor_ne_nb describe memory from each tensor's
+    dtype; a b or out that is not float32, an a whose dtype does not match
+    a_type, and tensors off the GPU are refused with ValueError before
+    anything reaches the library."""
+    import torch
+    a = torch.zeros(512, 8)
+    b = torch.zeros(512, 2560)
+    out = torch.zeros(2560, 8)
+    ne, nb = B.tensor_ne_nb(a, synth.F32, b, out)
+    assert ne == [8, 512, 1, 1, 2560, 512, 1, 1, 8, 2560, 1, 1]
+    assert nb[:2] == [4, 32] and nb[4:6] == [4, 4 * 2560] and nb[8:10] == [4, 32]
+    for bad_b in (b.half(), b.bfloat16(), b.double()):
+        with pytest.raises(ValueError, match="b must be float32"):
+            B.tensor_ne_nb(a, synth.F32, bad_b, out)
+    with pytest.raises(ValueError, match="out must be float32"):
+        B.tensor_ne_nb(a, synth.F32, b, out.half())
+    with pytest.raises(ValueError, match="a has dtype"):
+        B.tensor_ne_nb(a.half(), synth.F32, b, out)
+    with pytest.raises(ValueError, match="a has dtype"):
+        B.tensor_ne_nb(a, synth.F16, b, out)
+    with pytest.raises(ValueError, match="a has dtype"):
+        B.tensor_ne_nb(a, synth.Q4_K, b, out)
+    # f16 a: byte strides from the 2-byte element size
+    ne, nb = B.tensor_ne_nb(a.half(), synth.F16, b, out)
+    assert nb[:2] == [2, 16]
+    # quantized a as packed bytes
+    qa = torch.zeros(512, 144, dtype=torch.uint8)
+    ne, nb = B.tensor_ne_nb(qa, synth.Q4_K, b, torch.zeros(2560, 256))
+    assert ne[0] == 256 and nb[:2] == [144, 144]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.out_prod_tensors(a, synth.F32, b, out)

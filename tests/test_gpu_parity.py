@@ -476,71 +476,6 @@ def test_split_k_operand_swapped_auto():
     assert oracle.check(gpu, ref, den, TOL)["ok"]
 
 
-def _hip():
-    import ctypes
-    lib = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
-    lib.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
-    return lib
-
-
-def test_split_k_in_graph_capture():
-    """A splitting call captured in a graph: on a stream that has never run a
-    splitting call, capture is refused with E_CAPTURE (nothing enqueued); after
-    one uncaptured call on that stream, every replay equals the eager result
-    (with eager work on the captured buffers between replays)."""
-    import ctypes
-    hip = _hip()
-    raw = ctypes.c_void_p()
-    assert hip.hipStreamCreate(ctypes.byref(raw)) == 0
-    try:
-        ext = torch.cuda.ExternalStream(raw.value)
-        for name in ("lora4B_dh", "lora4B_dxW"):
-            inst = synth.workload(name)
-            plan = B.out_prod_plan(0x10000000, inst.a_type, 0x40000000000, 0x80000000000, inst.ne, inst.nb)
-            assert plan["splits"] > 1
-            a_d = G.to_dev(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1))
-            b_d = G.to_dev(inst.b)
-            eager = torch.empty(inst.dst_shape, dtype=torch.float32, device="cuda:0")
-            out = torch.zeros_like(eager)
-            B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), eager.data_ptr(), inst.ne, inst.nb,
-                       torch.cuda.current_stream().cuda_stream)
-            torch.cuda.synchronize()
-            ref = eager.cpu().numpy()
-            args = (a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb)
-            if name == "lora4B_dh":
-                g0 = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g0, stream=ext):
-                    out.zero_()
-                    st = B.out_prod_status(*args, raw.value)
-                assert B.STATUS[st] == "E_CAPTURE"
-                del g0
-                torch.cuda.synchronize()
-                ext.wait_stream(torch.cuda.current_stream())
-                B.out_prod(*args, raw.value)   # uncaptured: allocates the stream's workspace
-                torch.cuda.synchronize()
-                assert np.array_equal(out.cpu().numpy(), ref)
-            g = torch.cuda.CUDAGraph()
-            ext.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.graph(g, stream=ext):
-                B.out_prod(*args, raw.value)
-            torch.cuda.synchronize()
-            scale = 1.0
-            for rep in range(4):
-                out.fill_(float("nan"))
-                torch.cuda.synchronize()
-                g.replay()
-                torch.cuda.synchronize()
-                assert np.array_equal(out.cpu().numpy(), ref * np.float32(scale)), (name, rep)
-                b_d.mul_(2.0)
-                scale *= 2.0
-            del g
-            torch.cuda.synchronize()
-    finally:
-        torch.cuda.synchronize()
-        hip.hipStreamDestroy(raw)
-
-
 # ---------------------------------------------------------------- every a type
 
 NEW_TYPES = [synth.F16, synth.BF16, synth.Q4_0, synth.Q4_1, synth.Q5_0, synth.Q5_1,

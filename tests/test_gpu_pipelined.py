@@ -84,26 +84,13 @@ def test_full_tiles_every_stage_count(cfg):
         assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], K, kt, res)
 
 
-def _order_n_fast(plan, M, nb01):
-    """The host's tile-order choice (i1 fastest within a slice), restated
-    here to pick shapes that take each order: strips read per XCD, each
-    distinct strip once, for a chunk of consecutive logical tiles."""
-    tm = -(-M // plan["tile_m"])
-    tn = -(-plan["tile_n_total"] // plan["tile_n"])
-    c = min((plan["grid"] + 7) // 8, tm * tn)
-    a_strip = (nb01 / M if nb01 > 0 else 4.0) * plan["tile_m"]
-    b_strip = 4.0 * plan["tile_n"]
-    m_fast = min(c, tm) * a_strip + (-(-c // tm)) * b_strip
-    n_fast = (-(-c // tn)) * a_strip + min(c, tn) * b_strip
-    return n_fast < m_fast
-
-
 @pytest.mark.parametrize("cfg", [8, 9, 14, 0, 4])
 def test_tile_order_both_ways(cfg):
-    """Grids whose tiles walk i1 fastest (tall a, few b tiles) and i0 fastest,
-    with broadcast slices, full and ragged tiles, for q4_K and f32 a."""
-    code = B.kernel_code(B.KERNEL_TILED, cfg)
-    orders = set()
+    """Both tile orders (i0 or i1 fastest within a slice), forced through
+    out_prod_ex and confirmed by the plan, on grids with broadcast slices,
+    full and ragged tiles, for q4_K and f32 a; the automatic choice takes
+    each order on some of these shapes."""
+    auto_orders = set()
     for a_type, M, N, dps2 in ((synth.Q4_K, 4352, 256, 2), (synth.Q4_K, 512, 1100, 2),
                                (synth.F32, 4400, 130, 3), (synth.F32, 300, 900, 1),
                                (synth.Q4_K, 8192, 512, 2)):
@@ -113,15 +100,19 @@ def test_tile_order_both_ways(cfg):
         a_d = G.to_dev(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1))
         b_d = G.to_dev(inst.b)
         d_d = torch.empty(G.dst_extent_floats(inst.ne, inst.nb), dtype=torch.float32, device="cuda:0")
-        plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne,
-                               inst.nb, code)
-        plan["tile_n_total"] = N
-        orders.add(_order_n_fast(plan, M, inst.nb[1]))
-        G.log("case order cfg", cfg, synth.TYPE_NAMES[a_type], M, N, dps2, "n_fast",
-              _order_n_fast(plan, M, inst.nb[1]))
-        gpu = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, code)
+        auto = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne,
+                               inst.nb, B.kernel_code(B.KERNEL_TILED, cfg))
+        auto_orders.add(auto["tile_order"])
         ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
-        res = oracle.check(gpu, ref, den, TOL)
-        assert np.isfinite(gpu).all()
-        assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], M, N, res)
-    assert orders == {True, False}, orders
+        for order in (0, 1):
+            code = B.kernel_code(B.KERNEL_TILED, cfg, None, order)
+            plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne,
+                                   inst.nb, code)
+            assert plan["tile_order"] == order
+            G.log("case order cfg", cfg, synth.TYPE_NAMES[a_type], M, N, dps2, "order", order,
+                  "auto", auto["tile_order"])
+            gpu = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, code)
+            res = oracle.check(gpu, ref, den, TOL)
+            assert np.isfinite(gpu).all()
+            assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], M, N, order, res)
+    assert auto_orders == {0, 1}, auto_orders
