@@ -52,6 +52,10 @@ COMPOSITE["a_types_5120x17408"] = list(synth.TYPE_SWEEP)
 # MUL_MAT_ID_BACK through q4_K experts: the up and down projections' input
 # gradients of one mixture-of-experts FFN (64 experts, 8 routed, 512 tokens).
 COMPOSITE["moe_back_q4_K"] = list(synth.MOE_WORKLOADS)
+# The rank-4/8/24 LoRA parameter gradients at the 4B's widths (b of 2560 and
+# 9216 columns, K = 512 tokens): one launch each, HBM-bound.
+COMPOSITE["lora_rank_r"] = ["lora_r4_2560", "lora_r8_2560", "lora_r24_2560",
+                            "lora_r4_9216", "lora_r8_9216", "lora_r24_9216"]
 DEFAULT_WORKLOAD = "q4_K_27B_both"
 
 # The pages' per-op float-staging times for the same q4_K x f32 shapes
@@ -65,14 +69,18 @@ PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0}
 # the kernel sources whose hash is recorded with it.
 MEASURED_TRAFFIC = {
     # profiles/tiled_q4K_27B_lora_backward.md: launch A 378.3 MB, launch B 472.2 MB
-    "q4_K_27B_both": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 425.25e6},
+    "q4_K_27B_both": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 425.25e6,
+                      "profile": "profiles/tiled_q4K_27B_lora_backward.md"},
     # profiles/lora_linear_backward_4B_27B.md: the tiled launches (split dx_W main kernel
     # and dx_A); the split's reduce kernel is reported there separately
-    "lora_4B_linear_backward": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 37.01e6},
+    "lora_4B_linear_backward": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 37.01e6,
+                                "profile": "profiles/lora_linear_backward_4B_27B.md"},
     # profiles/column_lora_rank_and_deltanet.md
-    "lora_r8_9216": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 19.40e6},
+    "lora_r8_9216": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 19.40e6,
+                     "profile": "profiles/column_lora_rank_and_deltanet.md"},
     # profiles/id_back_moe_q4_K.md: the grouped tiled launches (routing kernels separate)
-    "moe_back_q4_K": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 172.65e6},
+    "moe_back_q4_K": {"kernel_hash": "2017d9ded78e32d8", "bytes_per_launch": 172.65e6,
+                      "profile": "profiles/id_back_moe_q4_K.md"},
 }
 
 
@@ -139,9 +147,24 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the benchmark: run a plain device copy of MB megabytes "
                          "5 times (the reference for scaling HBM byte counters)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of the benchmark: measure the device's sustained fp32 MFMA, "
+                         "HBM read and HBM copy rates and print them as JSON")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the short in-run measurement of the sustained peaks")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="instead of the benchmark: time cold single-launch reads of the "
+                         "workload's b (each f32 launch of it) in every strip decomposition of "
+                         "the read-floor probe, and print the fastest per launch as JSON")
     args = ap.parse_args()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.peaks:
+        print(json.dumps(measure_peaks(verbose=True)), flush=True)
+        return
+    if args.read_floor:
+        read_floor(args.workload, args.steps)
         return
 
     if args.gpus != 1:
@@ -300,15 +323,38 @@ def main():
     mt = MEASURED_TRAFFIC.get(args.workload)
     if mt and mt.get("kernel_hash") == src_hash:
         traffic = int(mt["bytes_per_launch"])
+        traffic_source = ("rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this workload, scaled "
+                          "by a 256 MB copy's counts, recorded for kernel source hash %s (%s)"
+                          % (src_hash, mt["profile"]))
+    elif mt:
+        traffic_source = ("none: the kernel sources (hash %s) changed since the counters were "
+                          "taken (hash %s)" % (src_hash, mt["kernel_hash"]))
+    else:
+        traffic_source = "none: no counter run recorded for this workload"
+    measured = None if args.no_peaks else measure_peaks()
     roofline = {
         "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-        "frac": round(achieved / peak, 4), "traffic": traffic,
+        "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_source": traffic_source,
         "kernel": dom,
         "launches_of_kernel": [insts[j].name for j in sel],
         "avg_launch_us": round(mean_s * 1e6, 3),
         "algorithmic_flops_per_launch": [int(x) for x in flops_launch],
         "algorithmic_bytes_per_launch": [int(x) for x in bytes_launch],
     }
+    if measured is not None:
+        mp = measured["mfma_f32_tflops"] if bound == "mfma" else measured["hbm_read_gbps"]
+        roofline["measured_peak"] = round(mp, 3)
+        roofline["frac_of_measured_peak"] = round(achieved / mp, 4)
+        roofline["measured_peak_note"] = (
+            "this device's sustained rate in the same run: %s" %
+            ("a loop of independent v_mfma_f32_32x32x2_f32" if bound == "mfma" else
+             "a 4 GiB streaming read"))
+
+    # NaN/Inf in the outputs of the last step (every launch's whole dst)
+    nonfinite = 0
+    for j in range(len(insts)):
+        d = sets[(K - 1) % R][j][2]
+        nonfinite += int(d.numel() - torch.isfinite(d).sum().item())
 
     value = flops_step / (ms_step * 1e-3) / 1e9
     gbps = bytes_step / (ms_step * 1e-3) / 1e9
@@ -344,11 +390,171 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": src_hash,
+        "git_rev": git_rev(),
+        "seeds": {i.name: int(i.seed) for i in insts},
+        "nonfinite_outputs": nonfinite,
+        "measured_peaks": measured,
     }
     if vs is not None:
         out["vs_baseline_note"] = ("ratio to the pages' float-staging per-op times for the same "
                                    "shapes on an Apple M5 (Metal): another machine, context only")
     print(json.dumps(out), flush=True)
+
+
+def git_rev():
+    """The checkout's commit (with "-dirty" for local changes), or None where
+    the tree carries no git metadata."""
+    import subprocess
+    try:
+        rev = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                             text=True, timeout=10)
+        if rev.returncode != 0:
+            return None
+        dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+        return rev.stdout.strip() + ("-dirty" if dirty.stdout.strip() else "")
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def load_calib():
+    import ctypes
+    import torch  # noqa: F401  (the HIP runtime torch loads must come first)
+    path = os.path.join(ROOT, "outer_product_gemm_amd", "libcalib.so")
+    if not os.path.exists(path):
+        raise SystemExit("libcalib.so is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.calib_mfma_f32.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.calib_read.argtypes = [vp, i64, vp, ctypes.c_int, vp]
+    lib.calib_copy.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.calib_strip_read.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, vp, vp]
+    return lib
+
+
+def _time_graph(fn, reps):
+    """Mean ms of one call of fn(stream_ptr), from `reps` calls captured in one
+    graph and replayed once (after one untimed replay)."""
+    import torch
+    dev = torch.device("cuda:0")
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    fn(cap.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        sp = torch.cuda.current_stream(dev).cuda_stream
+        for _ in range(reps):
+            fn(sp)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream(dev)
+    t0.record(st)
+    g.replay()
+    t1.record(st)
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / reps
+
+
+def measure_peaks(verbose=False):
+    """Sustained rates of this device, each from a graph of back-to-back
+    launches timed with HIP events: fp32 MFMA (2048 workgroups x 4 waves, each
+    wave 4 independent v_mfma_f32_32x32x2_f32 chains of 2048 steps: 275 GFLOP
+    per launch), a 4 GiB streaming read, and a 1 GiB device copy (counted as
+    read + write bytes)."""
+    import torch
+    lib = load_calib()
+    dev = torch.device("cuda:0")
+    grid, iters = 2048, 2048
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    flops = grid * 4 * iters * 4 * 4096
+    ms = _time_graph(lambda sp: lib.calib_mfma_f32(out.data_ptr(), grid, iters, sp), 10)
+    mfma = flops / (ms * 1e-3) / 1e12
+    n_read = (4 << 30) // 16
+    src = torch.ones(n_read * 4, dtype=torch.float32, device=dev)
+    rgrid = 256 * 16
+    rout = torch.empty(rgrid * 256, dtype=torch.float32, device=dev)
+    ms_r = _time_graph(lambda sp: lib.calib_read(src.data_ptr(), n_read, rout.data_ptr(), rgrid, sp), 10)
+    read = n_read * 16 / (ms_r * 1e-3) / 1e9
+    n_copy = (1 << 30) // 16
+    dst = torch.empty(n_copy * 4, dtype=torch.float32, device=dev)
+    ms_c = _time_graph(lambda sp: lib.calib_copy(src.data_ptr(), dst.data_ptr(), n_copy, rgrid, sp), 10)
+    copy = 2 * n_copy * 16 / (ms_c * 1e-3) / 1e9
+    del src, dst, out, rout
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    res = {"mfma_f32_tflops": mfma, "mfma_ms": ms, "hbm_read_gbps": read, "read_ms": ms_r,
+           "hbm_copy_gbps": copy, "copy_ms": ms_c,
+           "datasheet": {"mfma_f32_tflops": PEAK_MFMA_F32_TFLOPS, "hbm_gbps": PEAK_HBM_GBPS}}
+    if verbose:
+        log("peaks: mfma %.1f TFLOP/s (%.3f ms), read %.0f GB/s (%.3f ms), copy %.0f GB/s (%.3f ms)"
+            % (mfma, ms, read, ms_r, copy, ms_c))
+    return res
+
+
+def read_floor(workload, reps):
+    """The read floor of each f32 launch of a workload: for its b ([K][N] fp32
+    rows), every strip decomposition of the probe (strips of 16-256 columns,
+    K ranges, 256 or 512 threads, 4-16 loads in flight per thread), each timed
+    as `reps` launches in a graph over rotating cold copies (enough for 600 MB,
+    past the 256 MB Infinity Cache).  Prints one JSON line: per launch, the
+    fastest configuration and the times of all."""
+    import torch
+    lib = load_calib()
+    dev = torch.device("cuda:0")
+    names = COMPOSITE.get(workload, [workload])
+    report, seen = [], set()
+    for name in names:
+        inst = make_instance(name)
+        if is_moe(inst) or inst.b_kt:
+            continue
+        ne = inst.ne
+        N, K = ne[4] * ne[6] * ne[7], ne[1]
+        if N > 65536 or (K, N) in seen:
+            continue
+        seen.add((K, N))
+        plane = 4 * N * K
+        R = max(2, int(np.ceil(600e6 / plane)))
+        bufs = [torch.randn(K, N, dtype=torch.float32, device=dev) for _ in range(R)]
+        results = []
+        for cols in (16, 32, 64, 128, 256):
+            if N % cols:
+                continue
+            for threads in (256, 512):
+                if cols // 4 > threads:
+                    continue
+                for krows in sorted({K, max(1, K // 2), max(1, K // 4), max(1, K // 8)}, reverse=True):
+                    wgs = (N // cols) * ((K + krows - 1) // krows)
+                    if wgs > 8192:
+                        continue
+                    for U in (4, 8, 16):
+                        out = torch.empty(wgs * threads, dtype=torch.float32, device=dev)
+                        it = [0]
+
+                        def fn(sp, cols=cols, threads=threads, krows=krows, U=U, out=out):
+                            b = bufs[it[0] % R]
+                            it[0] += 1
+                            rc = lib.calib_strip_read(b.data_ptr(), 4 * N, K, N, cols, krows, threads, U,
+                                                      out.data_ptr(), sp)
+                            if rc != 0:
+                                raise RuntimeError("calib_strip_read %d" % rc)
+                        ms = _time_graph(fn, reps)
+                        results.append({"cols": cols, "threads": threads, "krows": krows, "U": U,
+                                        "workgroups": wgs, "us": round(ms * 1e3, 3)})
+        results.sort(key=lambda r: r["us"])
+        best = results[0]
+        log("%s: b %d x %d (%.2f MB): fastest %s; %.0f GB/s" % (
+            name, K, N, plane / 1e6, best, plane / (best["us"] * 1e-6) / 1e9))
+        report.append({"name": name, "K": K, "N": N, "b_bytes": plane, "best": best,
+                       "best_gbps": round(plane / (best["us"] * 1e-6) / 1e9, 1),
+                       "all": results})
+        del bufs
+        torch.cuda.empty_cache()
+    print(json.dumps({"read_floor": report}), flush=True)
 
 
 def copy_calibration(mb):

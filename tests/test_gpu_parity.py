@@ -120,11 +120,18 @@ def test_rank1_K1_bit_exact():
         assert np.array_equal(gpu[0, 0], expect)
 
 
+# The benchmarked q8_0 and q4_K launches: their whole output is checked
+# (the oracle needs a few seconds per launch on the host's cores).
+WHOLE_OUTPUT = ("q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120")
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_full_size(name):
-    """Every workload at its full size, auto kernel choice (the bench's launch)."""
+    """Every workload at its full size, auto kernel choice (the bench's launch);
+    every dst element of the q8_0 and q4_K 27B launches, sampled dst columns of
+    the other 5120 x 17408 type-sweep launches."""
     inst = synth.workload(name)
-    big = inst.ne[0] * inst.ne[1] * inst.ne[4] > 5e9
+    big = inst.ne[0] * inst.ne[1] * inst.ne[4] > 5e9 and name not in WHOLE_OUTPUT
     cols = None
     if big:
         rng = np.random.default_rng(seed_of(name))
@@ -156,7 +163,8 @@ def test_integer_exact_f32(a_ne, b_ne, kernel):
 @pytest.mark.parametrize("name", ["q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120"])
 def test_integer_exact_quant(name):
     """d = dmin = 1 and b in {-1, 0, 1}: every partial sum is an integer below
-    2^24, so the GPU must equal the oracle bit for bit at the full shape."""
+    2^24, so the GPU must equal the oracle bit for bit at the full shape, on
+    every dst element."""
     a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
     rng = synth.rng_for(seed_of("intq", name))
     one = int(synth.fp16_bits([1.0])[0])
@@ -169,10 +177,8 @@ def test_integer_exact_quant(name):
     ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
     G.log("int-exact", name)
     gpu = G.run(a, a_type, b, ne, nb)
-    cols = np.array([[i1, 0, 0] for i1 in (0, 1, 511, 777, b_ne[0] - 1)])
-    ref, _ = oracle.out_prod(a, a_type, b, ne, nb, cols=cols)
-    for j, (i1, _, _) in enumerate(cols):
-        assert np.array_equal(gpu[0, 0, i1], ref[j].astype(np.float32)), i1
+    ref, _ = oracle.out_prod(a, a_type, b, ne, nb)
+    assert np.array_equal(gpu, ref.astype(np.float32))
 
 
 @pytest.mark.parametrize("name", ["q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120"])
