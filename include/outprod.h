@@ -133,6 +133,8 @@ extern "C" {
                                     release under capture */
 #define OUTPROD_E_WORKSPACE (-14) /* the call needs a workspace and the device's 4 are
                                      bound to other streams */
+#define OUTPROD_E_SCRATCH (-15)  /* out_prod_noalloc: the plan's split partials exceed the
+                                    32 MiB static scratch */
 
 /*
  * out_prod: dst = OUT_PROD(a, b) as defined above, enqueued on `stream`.
@@ -260,6 +262,25 @@ int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int
                           outprod_plan *plan);
 
 /*
+ * out_prod_noalloc: out_prod that allocates nothing, for callers that cannot
+ * call hipMalloc -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, checks, plan and result
+ * (bit for bit) as out_prod.  A plan that splits K keeps its partials in a
+ * 32 MiB scratch array that the library's device image holds on each device
+ * (from the first use of the library there until the process ends) instead
+ * of a workspace of the pool; a plan whose partials exceed 32 MiB returns
+ * OUTPROD_E_SCRATCH before any HIP call, with dst untouched.  Nothing in the
+ * scratch needs clearing: a split writes every partial it reads.
+ * The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress); make it outside capture.  Every call on a device
+ * shares that device's scratch: splitting calls whose work overlaps on one
+ * GPU (other streams, concurrent graph replays) race and must be ordered by
+ * the caller.  Calls that do not split K use no scratch.
+ */
+int out_prod_noalloc(const void *a, int a_type, const float *b, float *dst,
+                     const int64_t ne[12], const int64_t nb[12], void *stream);
+
+/*
  * out_prod_release_stream: free the workspace bound to `stream` (a
  * hipStream_t; NULL = the current device's default stream), if any, after
  * waiting for the work queued on `stream` (hipStreamSynchronize).  Call it
@@ -282,8 +303,8 @@ int out_prod_workspace_count(int *count);
 /* A static English description of a status code; never NULL. */
 const char *out_prod_strerror(int status);
 
-/* Library ABI version: 3 (2 had no tile_order in outprod_plan and no
- * workspace pool calls; 1 had no split fields). */
+/* Library ABI version: 3 (2 had no tile_order in outprod_plan, no workspace
+ * pool calls and no out_prod_noalloc; 1 had no split fields). */
 int out_prod_version(void);
 
 #ifdef __cplusplus

@@ -37,7 +37,7 @@ OUTPROD_OK = 0
 STATUS = {
     -1: "E_NULL", -2: "E_TYPE", -3: "E_SHAPE", -4: "E_K", -5: "E_DST_SHAPE", -6: "E_BCAST",
     -7: "E_QK", -8: "E_LAYOUT", -9: "E_ALIAS", -10: "E_RANGE", -11: "E_KERNEL", -12: "E_HIP",
-    -13: "E_CAPTURE", -14: "E_WORKSPACE",
+    -13: "E_CAPTURE", -14: "E_WORKSPACE", -15: "E_SCRATCH",
 }
 KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
@@ -58,7 +58,7 @@ ABI_VERSION = 3
 
 # Every symbol the header declares.
 EXPORTS = ("out_prod", "out_prod_ex", "out_prod_plan", "out_prod_id_back", "out_prod_id_back_ex",
-           "out_prod_id_back_plan", "out_prod_release_stream", "out_prod_workspace_count",
+           "out_prod_id_back_plan", "out_prod_noalloc", "out_prod_release_stream", "out_prod_workspace_count",
            "out_prod_strerror", "out_prod_version")
 _I64x16 = ctypes.c_int64 * 16
 
@@ -111,6 +111,8 @@ def load_library(path: str = LIB_PATH):
             lib.out_prod_id_back_plan.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64p, i64p,
                                                   ctypes.c_int, ctypes.POINTER(outprod_plan)]
             lib.out_prod_id_back_plan.restype = ctypes.c_int
+            lib.out_prod_noalloc.argtypes = [vp, ctypes.c_int, vp, vp, i64p, i64p, vp]
+            lib.out_prod_noalloc.restype = ctypes.c_int
             lib.out_prod_release_stream.argtypes = [vp]
             lib.out_prod_release_stream.restype = ctypes.c_int
             lib.out_prod_workspace_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
@@ -177,6 +179,20 @@ def out_prod_ex(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0,
     """C ``out_prod_ex``: out_prod with the kernel family forced."""
     _check(load_library().out_prod_ex(a or None, int(a_type), b or None, dst or None,
                                       _arr12(ne), _arr12(nb), stream or None, int(kernel)))
+
+
+def out_prod_noalloc(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0) -> None:
+    """C ``out_prod_noalloc``: out_prod that allocates nothing (split partials
+    in the library's static device scratch).  Raises OutProdError on a
+    nonzero status."""
+    _check(load_library().out_prod_noalloc(a or None, int(a_type), b or None, dst or None,
+                                           _arr12(ne), _arr12(nb), stream or None))
+
+
+def out_prod_noalloc_status(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0) -> int:
+    """``out_prod_noalloc`` returning the raw status instead of raising."""
+    return int(load_library().out_prod_noalloc(a or None, int(a_type), b or None, dst or None,
+                                               _arr12(ne), _arr12(nb), stream or None))
 
 
 def out_prod_status(a: int, a_type: int, b: int, dst: int, ne, nb, stream: int = 0,

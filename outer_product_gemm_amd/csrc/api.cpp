@@ -76,12 +76,6 @@ bool overlaps(const void *p, int64_t np, const void *q, int64_t nq) {
     return a0 < b1 && b0 < a1;
 }
 
-struct Checked {
-    Problem p;
-    Launch l;
-    bool swapped;
-};
-
 // The same OUT_PROD with the roles of a and b exchanged: dst^T = a'·b'^T with
 // a' = b, b' = a, so dst element (i0, i1) is element (i1, i0) of the swapped
 // problem (dst strides exchanged).  Used for a narrow f32 b (ne10 <= 32) with a
@@ -110,11 +104,13 @@ Problem swap_operands(const Problem &p) {
     return q;
 }
 
+}  // namespace
+
 // no_split: plan without a K split unless one is forced (for a call that
 // has no workspace).
 int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
                       const int64_t *ne, const int64_t *nb, int kernel, Checked *c,
-                      bool no_split = false) {
+                      bool no_split) {
     if (!ne || !nb) return OUTPROD_E_NULL;
     if (block_bytes(a_type) == 0) return OUTPROD_E_TYPE;
     for (int i = 0; i < 12; ++i)
@@ -289,6 +285,34 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     return OUTPROD_OK;
 }
 
+hipError_t enqueue(Checked &c, hipStream_t s, uint8_t *ws) {
+    if (c.l.splits > 1) {
+        c.p.splits = c.l.splits;
+        c.p.ksplit = c.l.ksplit;
+        c.p.ws = ws;
+    }
+    hipError_t e = hipSuccess;
+    switch (c.l.kernel) {
+    case OUTPROD_KERNEL_NONE:
+        return hipSuccess;
+    case OUTPROD_KERNEL_ZERO:
+        e = launch_zero(c.p, c.l, s);
+        break;
+    case OUTPROD_KERNEL_SKINNY:
+        e = launch_skinny(c.p, c.l, s);
+        break;
+    case OUTPROD_KERNEL_TILED:
+        e = launch_tiled(c.p, c.l, s);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    if (e == hipSuccess && c.p.splits > 1) e = launch_split_reduce(c.p, s);
+    return e;
+}
+
+namespace {
+
 // The library's workspaces (split-K partials, MUL_MAT_ID_BACK routing
 // tables): at most kMaxWorkspaces per device, kWorkspaceBytes each, each
 // bound to one stream.  A stream's first call that needs one allocates it
@@ -361,8 +385,8 @@ int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne
     int rc = validate_and_plan(a, a_type, b, dst, ne, nb, kernel, &c);
     if (rc != OUTPROD_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = nullptr;
     if (c.l.splits > 1) {
-        uint8_t *ws = nullptr;
         rc = stream_workspace(s, &ws);
         if (rc == OUTPROD_E_CAPTURE || rc == OUTPROD_E_WORKSPACE) {
             // no workspace for this stream: an automatic plan runs unsplit
@@ -372,30 +396,9 @@ int run(const void *a, int a_type, const float *b, float *dst, const int64_t *ne
             if (rc != OUTPROD_OK) return rc;
         } else if (rc != OUTPROD_OK) {
             return rc;
-        } else {
-            c.p.splits = c.l.splits;
-            c.p.ksplit = c.l.ksplit;
-            c.p.ws = ws;
         }
     }
-    hipError_t e = hipSuccess;
-    switch (c.l.kernel) {
-    case OUTPROD_KERNEL_NONE:
-        return OUTPROD_OK;
-    case OUTPROD_KERNEL_ZERO:
-        e = launch_zero(c.p, c.l, s);
-        break;
-    case OUTPROD_KERNEL_SKINNY:
-        e = launch_skinny(c.p, c.l, s);
-        break;
-    case OUTPROD_KERNEL_TILED:
-        e = launch_tiled(c.p, c.l, s);
-        break;
-    default:
-        return OUTPROD_E_KERNEL;
-    }
-    if (e == hipSuccess && c.p.splits > 1) e = launch_split_reduce(c.p, s);
-    return e == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
+    return enqueue(c, s, ws) == hipSuccess ? OUTPROD_OK : OUTPROD_E_HIP;
 }
 
 // ---------------------------------------------------------------- MUL_MAT_ID_BACK
@@ -659,6 +662,8 @@ const char *out_prod_strerror(int status) {
     case OUTPROD_E_CAPTURE:
         return "the call needs a workspace, the stream is capturing a graph and has none "
                "bound (or a release under capture): make one uncaptured call on this stream first";
+    case OUTPROD_E_SCRATCH:
+        return "the plan's split partials exceed out_prod_noalloc's 32 MiB static scratch";
     case OUTPROD_E_WORKSPACE:
         return "the device's workspaces (4) are all bound to other streams: release a stream "
                "that no longer needs one with out_prod_release_stream";

@@ -62,6 +62,24 @@ struct Launch {
                       // 1 = i1 fastest; on entry to plan_tiled, -1 = automatic
 };
 
+// A validated OUT_PROD call and its plan.  swapped: the problem runs with
+// the operands exchanged (a narrow f32 b with a wide f32 a).
+struct Checked {
+    Problem p;
+    Launch l;
+    bool swapped;
+};
+
+// Every host-side check of the contract, then the plan (no HIP call).
+// kernel: out_prod_ex's override code (0 = automatic); no_split: plan
+// without a K split unless one is forced.  Returns OUTPROD_OK or a status.
+int validate_and_plan(const void *a, int a_type, const float *b, const float *dst,
+                      const int64_t *ne, const int64_t *nb, int kernel, Checked *c,
+                      bool no_split = false);
+// Enqueue a validated plan on stream s; ws: the split's partials
+// (split_bytes(c.p, c.l.splits) bytes), unused without a split.
+hipError_t enqueue(Checked &c, hipStream_t s, uint8_t *ws);
+
 // One validated MUL_MAT_ID_BACK problem: for routed slot s = i + n_used*t,
 // dst row (i, t) = expert ids[i,t] (ne00 x K, rows of ne00 values along K)
 // times the slot's gradient column g[:, i, t] (K contiguous floats).
