@@ -96,14 +96,27 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash():
-    """Hash of the code (not the comments) of every kernel and host source."""
+# The sources each kernel family's code and launch plan come from (the host
+# file api.cpp chooses the plan; the family files hold the kernels).
+FAMILY_SOURCES = {
+    "tiled": ["api.cpp", "outprod_internal.h", "kernel_common.h", "block_formats.h", "tiled_impl.h",
+              "kernel_tiled.hip", "tiled_f32.hip", "tiled_half.hip", "tiled_q8.hip", "tiled_q45.hip",
+              "tiled_k4.hip", "tiled_k.hip", "kernel_reduce.hip"],
+    "skinny": ["api.cpp", "outprod_internal.h", "kernel_common.h", "kernel_skinny.hip",
+               "kernel_reduce.hip"],
+}
+FAMILY_SOURCES["tiled_id"] = FAMILY_SOURCES["tiled"] + ["kernel_id_back.hip"]
+
+
+def kernel_source_hash(files=None):
+    """Hash of the code (not the comments) of the given csrc files (default:
+    every kernel and host source)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "outer_product_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update((name + "\n" + _code_only(f.read())).encode())
+    names = sorted(files) if files else sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".cpp")))
+    for name in names:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update((name + "\n" + _code_only(f.read())).encode())
     return h.hexdigest()[:16]
 
 
@@ -186,14 +199,22 @@ def main():
     work = [algorithmic(i) for i in insts]
     flops_step = sum(w[0] for w in work)
     bytes_step = sum(w[1] for w in work)
-    set_bytes = sum(i.a.nbytes + (i.g.nbytes + i.ids.nbytes if is_moe(i) else i.b.nbytes) +
-                    4 * int(np.prod(i.dst_shape)) for i in insts)
-    R = args.rotate or max(1, min(256, int(np.ceil(600e6 / set_bytes))))
+    launch_bytes = [i.a.nbytes + (i.g.nbytes + i.ids.nbytes if is_moe(i) else i.b.nbytes) +
+                    4 * int(np.prod(i.dst_shape)) for i in insts]
+    set_bytes = sum(launch_bytes)
+    # Each launch rotates over enough copies of its own inputs (>= 600 MB of
+    # them) that every timed launch, also in the per-launch pass below, reads
+    # them from HBM rather than the 256 MB Infinity Cache.
+    if args.rotate:
+        copies_n = [args.rotate] * len(insts)
+    else:
+        copies_n = [max(1, min(256, int(np.ceil(600e6 / nb_)))) for nb_ in launch_bytes]
+    R = max(copies_n)
 
-    sets = []
-    for r in range(R):
-        bufs = []
-        for inst in insts:
+    copies = []
+    for j, inst in enumerate(insts):
+        cj = []
+        for r in range(copies_n[j]):
             a_d = torch.from_numpy(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1)).to(dev)
             if is_moe(inst):
                 g_d = torch.from_numpy(inst.g).to(dev)
@@ -202,18 +223,20 @@ def main():
                 plan = B.out_prod_id_back_plan(a_d.data_ptr(), inst.a_type, g_d.data_ptr(),
                                                i_d.data_ptr(), d_d.data_ptr(), inst.ne, inst.nb)
                 plan["kernel_name"] = "tiled_id"
-                bufs.append((a_d, (g_d, i_d), d_d, plan))
+                cj.append((a_d, (g_d, i_d), d_d, plan))
                 continue
             b_d = torch.from_numpy(inst.b).to(dev)
             d_d = torch.empty(inst.dst_shape, dtype=torch.float32, device=dev)
             plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(),
                                    inst.ne, inst.nb)
-            bufs.append((a_d, b_d, d_d, plan))
-        sets.append(bufs)
+            cj.append((a_d, b_d, d_d, plan))
+        copies.append(cj)
+    # sets[r][j]: launch j's inputs for step r
+    sets = [[copies[j][r % copies_n[j]] for j in range(len(insts))] for r in range(R)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
-    log("rotating sets", R, "set MB %.1f" % (set_bytes / 1e6),
+    log("rotating copies per launch", copies_n, "set MB %.1f" % (set_bytes / 1e6),
         "plans", [(p[3]["kernel_name"], p[3]["tile_m"], p[3]["tile_n"], p[3]["grid"]) for p in sets[0]])
 
     def launch(r, j, stream_ptr):
@@ -319,16 +342,18 @@ def main():
         achieved = float(bytes_launch.mean()) / mean_s / 1e9
         peak, unit = PEAK_HBM_GBPS, "GB/s"
     src_hash = kernel_source_hash()
+    fam_hash = kernel_source_hash(FAMILY_SOURCES.get(dom))
     traffic = None
     mt = MEASURED_TRAFFIC.get(args.workload)
-    if mt and mt.get("kernel_hash") == src_hash:
+    if mt and mt.get("kernel_hash") == fam_hash:
         traffic = int(mt["bytes_per_launch"])
-        traffic_source = ("rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this workload, scaled "
-                          "by a 256 MB copy's counts, recorded for kernel source hash %s (%s)"
-                          % (src_hash, mt["profile"]))
+        traffic_source = ("rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this workload (L2-to-"
+                          "memory bytes, Infinity Cache hits included), scaled by a 256 MB copy's "
+                          "counts, recorded for the %s kernel sources with hash %s (%s)"
+                          % (dom, fam_hash, mt["profile"]))
     elif mt:
-        traffic_source = ("none: the kernel sources (hash %s) changed since the counters were "
-                          "taken (hash %s)" % (src_hash, mt["kernel_hash"]))
+        traffic_source = ("none: the %s kernel sources (hash %s) changed since the counters were "
+                          "taken (hash %s)" % (dom, fam_hash, mt["kernel_hash"]))
     else:
         traffic_source = "none: no counter run recorded for this workload"
     measured = None if args.no_peaks else measure_peaks()
@@ -383,13 +408,14 @@ def main():
                           "kernel": p[3]["kernel_name"], "variant": p[3]["variant"],
                           "swapped": bool(p[3].get("swapped", 0)), "us": round(u, 3)}
                          for i, p, u in zip(insts, sets[0], launch_us)],
-            "rotating_input_sets": R,
+            "rotating_input_copies": copies_n,
         },
         "gbps": round(gbps, 1),
         "ms_per_step_eager": round(ms_eager, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": src_hash,
+        "kernel_family_hash": fam_hash,
         "git_rev": git_rev(),
         "seeds": {i.name: int(i.seed) for i in insts},
         "nonfinite_outputs": nonfinite,

@@ -179,8 +179,10 @@ typedef struct outprod_plan {
     int64_t ksplit;   /* K rows per range (the last range may be shorter) */
     int64_t workspace_bytes; /* partial results: splits * ne00 * ne10 * slices * 4
                                 (0 without a split); at most 64 MiB */
-    int tile_order;   /* tiled kernel: 0 = consecutive workgroups walk i0 fastest
-                         within a slice, 1 = i1 fastest; -1 for other kernels */
+    int group_m;      /* tiled kernel: consecutive workgroups walk the tiles of a
+                         slice in groups of group_m tiles along i0 (i0 fastest
+                         within a group, then i1): tiles along i0 = i0 fastest,
+                         1 = i1 fastest; 0 for other kernels */
     int reserved;     /* 0 */
 } outprod_plan;
 
@@ -204,12 +206,12 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
  * the split count of K (with a forced family only): 1 = no split, n = n
  * ranges of ceil(K/n) rows (fewer when K is short); 0 lets the library
  * choose.  Bits 24-30 may force the tiled kernel's tile order (with the
- * TILED family only): (order + 1) << 24 with the order as reported in
- * outprod_plan.tile_order; 0 lets the library choose.  A family,
- * configuration, split or order that cannot run the problem returns
- * OUTPROD_E_KERNEL (e.g. SKINNY for a quantized a, an unknown configuration
- * index, more ranges than K rows, partials beyond the workspace, an order
- * with another family).
+ * TILED family only): group_m << 24, 1 <= group_m <= 127 (larger than the
+ * tiles along i0 means i0 fastest), as reported in outprod_plan.group_m; 0
+ * lets the library choose.  A family, configuration, split or order that
+ * cannot run the problem returns OUTPROD_E_KERNEL (e.g. SKINNY for a
+ * quantized a, an unknown configuration index, more ranges than K rows,
+ * partials beyond the workspace, an order with another family).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);
@@ -303,7 +305,7 @@ int out_prod_workspace_count(int *count);
 /* A static English description of a status code; never NULL. */
 const char *out_prod_strerror(int status);
 
-/* Library ABI version: 3 (2 had no tile_order in outprod_plan, no workspace
+/* Library ABI version: 3 (2 had no group_m in outprod_plan, no workspace
  * pool calls and no out_prod_noalloc; 1 had no split fields). */
 int out_prod_version(void);
 

@@ -43,14 +43,15 @@ KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3,
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
 
 
-def kernel_code(family: int, config: int = None, splits: int = None, order: int = None) -> int:
+def kernel_code(family: int, config: int = None, splits: int = None, group_m: int = None) -> int:
     """out_prod_ex's kernel argument: a family, optionally with a forced
     configuration index (as reported by out_prod_plan's ``variant``), a
     forced split count of K (1 = no split) and a forced tile order of the
-    tiled kernel (as reported by out_prod_plan's ``tile_order``)."""
+    tiled kernel: tiles walk groups of ``group_m`` (1-127) tiles along i0 (as
+    reported by out_prod_plan's ``group_m``)."""
     code = family | ((config + 1) << 8 if config is not None else 0)
     code |= splits << 16 if splits is not None else 0
-    return code | ((order + 1) << 24 if order is not None else 0)
+    return code | (group_m << 24 if group_m is not None else 0)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboutprod.so")
 # The library ABI this binding's structures and signatures match.
@@ -75,7 +76,7 @@ class outprod_plan(ctypes.Structure):
                 ("grid", ctypes.c_int64), ("slices", ctypes.c_int64), ("dps2", ctypes.c_int64),
                 ("dps3", ctypes.c_int64), ("flops", ctypes.c_int64), ("variant", ctypes.c_int),
                 ("swapped", ctypes.c_int), ("splits", ctypes.c_int), ("ksplit", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64), ("tile_order", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_int64), ("group_m", ctypes.c_int),
                 ("reserved", ctypes.c_int)]
 
 

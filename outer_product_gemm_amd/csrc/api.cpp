@@ -232,18 +232,16 @@ int validate_and_plan(const void *a, int a_type, const float *b, const float *ds
     }
 
     // kernel = family | (tile configuration + 1) << 8 | splits << 16 |
-    // (tile order + 1) << 24; configuration 0, splits 0 and order 0 =
-    // automatic
+    // group_m << 24; configuration 0, splits 0 and group_m 0 = automatic
     const int variant = (kernel >> 8) & 0xFF;
     const int splits = (kernel >> 16) & 0xFF;
-    const int order = (kernel >> 24) & 0x7F;
-    if (order > 2) return OUTPROD_E_KERNEL;
+    const int group_m = (kernel >> 24) & 0x7F;
     kernel &= 0xFF;
     if ((variant != 0 || splits != 0) && kernel != OUTPROD_KERNEL_TILED &&
         kernel != OUTPROD_KERNEL_SKINNY)
         return OUTPROD_E_KERNEL;
-    if (order != 0 && kernel != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
-    l.order = order - 1;
+    if (group_m != 0 && kernel != OUTPROD_KERNEL_TILED) return OUTPROD_E_KERNEL;
+    l.group_m = group_m;
     l.variant = variant;
     l.splits = splits == 0 && no_split ? 1 : splits;
     bool ok;
@@ -587,7 +585,7 @@ int out_prod_id_back_plan(const void *as, int as_type, const float *g, const int
     plan->splits = 1;
     plan->ksplit = c.p.K;
     plan->workspace_bytes = c.l.kernel == OUTPROD_KERNEL_TILED ? outprod::id_workspace_bytes(c.p) : 0;
-    plan->tile_order = -1;
+    plan->group_m = 0;
     return OUTPROD_OK;
 }
 
@@ -625,7 +623,7 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
     plan->splits = c.l.splits > 1 ? c.l.splits : 1;
     plan->ksplit = c.l.splits > 1 ? c.l.ksplit : c.p.K;
     plan->workspace_bytes = outprod::split_bytes(c.p, plan->splits);
-    plan->tile_order = c.l.kernel == OUTPROD_KERNEL_TILED ? c.l.order : -1;
+    plan->group_m = c.l.kernel == OUTPROD_KERNEL_TILED ? c.l.group_m : 0;
     return OUTPROD_OK;
 }
 

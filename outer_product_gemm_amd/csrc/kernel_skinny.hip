@@ -58,18 +58,25 @@ __device__ __forceinline__ void load_cols(const uint8_t *row, int col, int N, fl
     }
 }
 
-// G consecutive floats of one row of a starting at column i0 (G = 1, 2, 4;
-// i0 a multiple of G).  FULL: a's rows are 16-byte aligned and M is a
+// G consecutive floats of one row of a starting at column i0 (G = 1, 2, 4,
+// 6, 8; i0 a multiple of G).  FULL: a's rows are 16-byte aligned and M is a
 // multiple of G, so a group is either wholly in range or wholly past the end:
-// one vector load at the clamped start min(i0, M-G), with no branch (callers
-// zero out-of-range values).  Otherwise element loads at clamped columns.
+// vector loads (float4 pieces when G % 4 == 0, else float2: the group's start
+// is then 8-byte aligned) at the clamped start min(i0, M-G), with no branch
+// (callers zero out-of-range values).  Otherwise element loads at clamped
+// columns.
 template <int G, bool FULL>
 __device__ __forceinline__ void load_a_group(const uint8_t *row, int i0, int M, float *out) {
     if constexpr (G > 1 && FULL) {
         const int ic = i0 < M - G ? i0 : M - G;
-        const typename VecF<G>::type v = *(const typename VecF<G>::type *)(row + (int64_t)ic * 4);
+        constexpr int P = G % 4 == 0 ? 4 : 2;
+        const uint8_t *src = row + (int64_t)ic * 4;
 #pragma unroll
-        for (int t = 0; t < G; ++t) out[t] = v[t];
+        for (int h = 0; h < G / P; ++h) {
+            const typename VecF<P>::type v = *(const typename VecF<P>::type *)(src + 4 * P * h);
+#pragma unroll
+            for (int t = 0; t < P; ++t) out[P * h + t] = v[t];
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < G; ++t) {
@@ -507,11 +514,14 @@ struct ColCfg {
 };
 // 16x16x4: 0: 16-col strips, 8 waves x 8 steps   1: 32-col, 8 x 8   2: 64-col, 8 x 8
 //          3: 32-col, 16 x 8   4: 64-col, 8 x 16   5: 16-col, 16 x 8
+//          11: 32-col, 8 x 16  12: 16-col, 8 x 16
 // 4x4x1:   6: 16-col, 8 x 16   7: 32-col, 8 x 16   8: 64-col, 8 x 16
 //          9: 32-col, 8 x 8    10: 64-col, 8 x 8
-constexpr ColCfg kColCfgs[] = {{16, 1, 8, 8}, {16, 2, 8, 8},  {16, 4, 8, 8}, {16, 2, 16, 8},
-                               {16, 4, 8, 16}, {16, 1, 16, 8}, {4, 1, 8, 16}, {4, 2, 8, 16},
-                               {4, 4, 8, 16},  {4, 2, 8, 8},   {4, 4, 8, 8}};
+// (8 waves x 16 steps x 4 rows: K = 512 in a single batch of loads per wave)
+constexpr ColCfg kColCfgs[] = {{16, 1, 8, 8}, {16, 2, 8, 8},  {16, 4, 8, 8},  {16, 2, 16, 8},
+                               {16, 4, 8, 16}, {16, 1, 16, 8}, {4, 1, 8, 16},  {4, 2, 8, 16},
+                               {4, 4, 8, 16},  {4, 2, 8, 8},   {4, 4, 8, 8},   {16, 2, 8, 16},
+                               {16, 1, 8, 16}};
 constexpr int kNumColCfgs = sizeof(kColCfgs) / sizeof(kColCfgs[0]);
 
 template <int MT, int C>
@@ -528,6 +538,8 @@ const void *col_fn(int c) {
     case 3: return col_fn<MT, 3>();
     case 4: return col_fn<MT, 4>();
     case 5: return col_fn<MT, 5>();
+    case 11: return col_fn<MT, 11>();
+    case 12: return col_fn<MT, 12>();
     default: return col_fn<MT, 0>();
     }
 }
@@ -540,24 +552,40 @@ const void *narrow_fn() {
 
 template <int T4>
 const void *narrow_fn(int c) {
-    switch (c) {
-    case 7: return narrow_fn<T4, 7>();
-    case 8: return narrow_fn<T4, 8>();
-    case 9: return narrow_fn<T4, 9>();
-    case 10: return narrow_fn<T4, 10>();
-    default: return narrow_fn<T4, 6>();
+    if constexpr (T4 > 4) {
+        // wide blocks of a only with strips of up to 32 columns (the LDS
+        // reduction of 64-column strips would exceed 160 KB)
+        switch (c) {
+        case 7: return narrow_fn<T4, 7>();
+        case 9: return narrow_fn<T4, 9>();
+        default: return narrow_fn<T4, 6>();
+        }
+    } else {
+        switch (c) {
+        case 7: return narrow_fn<T4, 7>();
+        case 8: return narrow_fn<T4, 8>();
+        case 9: return narrow_fn<T4, 9>();
+        case 10: return narrow_fn<T4, 10>();
+        default: return narrow_fn<T4, 6>();
+        }
     }
 }
 
-// 4-column blocks of a per workgroup for the narrow kernel (at most 16
-// columns of a; wider a takes several i0 blocks)
-int narrow_t4(int64_t M) { return M <= 4 ? 1 : M <= 8 ? 2 : 4; }
+// 4-column blocks of a per workgroup for the narrow kernel: an a up to 32
+// columns wide in one i0 block (rank 24 as 6 blocks, not 2 x 4 with 8
+// columns of padding); 64-column strips (cw 4) take at most 16 columns per
+// block, wider a in several i0 blocks.
+int narrow_t4(int64_t M, int cw) {
+    return M <= 4 ? 1 : M <= 8 ? 2 : (M <= 16 || cw > 2) ? 4 : M <= 24 ? 6 : 8;
+}
 
 const void *narrow_dispatch(int t4, int c) {
     switch (t4) {
     case 1: return narrow_fn<1>(c);
     case 2: return narrow_fn<2>(c);
-    default: return narrow_fn<4>(c);
+    case 4: return narrow_fn<4>(c);
+    case 6: return narrow_fn<6>(c);
+    default: return narrow_fn<8>(c);
     }
 }
 
@@ -613,7 +641,7 @@ bool plan_skinny(const Problem &p, Launch *l) {
     const int64_t col_blocks = (p.N + cols - 1) / cols;
     int tile_m;
     if (c.mma == 4) {
-        tile_m = 4 * narrow_t4(p.M);
+        tile_m = 4 * narrow_t4(p.M, c.cw);
     } else {
         tile_m = p.M > 16 ? 32 : 16;
     }

@@ -106,36 +106,81 @@ bool plan_tiled(const Problem &p, Launch *l) {
     l->splits = best_splits;
     l->ksplit = best_splits > 1 ? ksplit : p.K;
     l->grid = tm * tn * p.ne12 * p.ne13 * best_splits;
-    if (l->order < 0) l->order = tile_order_n_fast(p, *l, tm, tn);
+    if (l->group_m <= 0) l->group_m = tile_group_m(p, *l, tm, tn);
+    if (l->group_m > tm) l->group_m = (int)tm;
     return true;
 }
 
-// Tile order within a slice.  Consecutive logical tiles run on one XCD
-// (xcd_remap), and each XCD has its own L2: walking i0 fastest has the XCDs
-// share b's strips while each reads most of a, walking i1 fastest the
-// reverse.  The order whose strips read per XCD (each distinct strip once,
-// per row of K) add up to fewer bytes is taken: the i0-fastest order reads
-// 473 MB per launch for m5120 k17408 n1024 q4_K in 160 x 128 tiles against
-// 472 MB estimated, 357 MB in 80 x 256 tiles against 342 MB; m17408 k5120
-// n1024 in 272 x 128 tiles reads 523 MB that way and 400 MB i1-fastest (the
-// estimate's 218 MB assumes each b strip stays in L2), in the same time.
-int tile_order_n_fast(const Problem &p, const Launch &l, int64_t tiles_m, int64_t tiles_n) {
+// Tile order within a slice: consecutive logical tiles walk groups of
+// group_m m-tiles (i0 fastest within a group, then i1, then the next group),
+// so group_m = tiles_m walks i0 fastest over the slice and group_m = 1 walks
+// i1 fastest.  Consecutive logical tiles run on one XCD (xcd_remap), whose
+// L2 (4 MB) is shared by the tiles it runs at once -- about one per CU, 32 --
+// and keeps little across rounds of tiles.  The estimate follows the
+// kernel's mapping over each XCD's first (up to 4) rounds of 32 tiles: per round, the
+// a strips (all of K, at a's stored size) of its distinct m-tiles plus the b
+// strips of its distinct n-tiles.  Candidates: i0 fastest and groups of 1,
+// 2, 4, ... m-tiles; the fewest bytes win (i0 fastest on ties).  Measured
+// per launch with FETCH_SIZE: m5120 k17408 n1024 q4_K in 80 x 256 tiles (one
+// round): 357 MB i0 fastest (estimate 342); m17408 k5120 in 272 x 128 tiles
+// (two rounds): 523 MB i0 fastest, 400 MB i1 fastest (estimates 442 and 384
+// MB); groups of 8 are estimated at 267 MB.
+namespace {
+int64_t tile_of(int64_t rem, int64_t g, int64_t tiles_m, int64_t tiles_n, int64_t *n) {
+    const int64_t gsize = g * tiles_n, grp = rem / gsize, idx = rem % gsize;
+    const int64_t gm = std::min(g, tiles_m - grp * g);
+    *n = idx / gm;
+    return grp * g + idx % gm;
+}
+}  // namespace
+
+int tile_group_m(const Problem &p, const Launch &l, int64_t tiles_m, int64_t tiles_n) {
     const int64_t per = tiles_m * tiles_n;
-    int64_t c = ((int64_t)l.grid + 7) / 8;  // logical tiles per XCD
-    if (c > per) c = per;
+    const int64_t chunk = ((int64_t)l.grid + 7) / 8;  // logical tiles per XCD
     const double a_strip = (p.nb01 > 0 ? (double)p.nb01 / (double)p.M : 4.0) * l.tile_m;
     const double b_strip = 4.0 * l.tile_n;
-    const double m_fast = (double)std::min(c, tiles_m) * a_strip + (double)((c + tiles_m - 1) / tiles_m) * b_strip;
-    const double n_fast = (double)((c + tiles_n - 1) / tiles_n) * a_strip + (double)std::min(c, tiles_n) * b_strip;
-    return n_fast < m_fast ? 1 : 0;
+    int64_t best = tiles_m;
+    double best_bytes = 0;
+    bool first = true;
+    int64_t cand[64];
+    int nc = 0;
+    cand[nc++] = tiles_m;
+    for (int64_t g = 1; g < tiles_m && nc < 64; g *= 2) cand[nc++] = g;
+    for (int ci = 0; ci < nc; ++ci) {
+        const int64_t g = cand[ci];
+        double bytes = 0;
+        for (int64_t x = 0; x < 8; ++x) {
+            const int64_t lo = x * chunk, hi = std::min<int64_t>((x + 1) * chunk, l.grid);
+            for (int64_t r0 = lo; r0 < hi && r0 < lo + 4 * 32; r0 += 32) {
+                int64_t ms[32], ns[32];
+                int cnt = 0;
+                for (int64_t t = r0; t < std::min(r0 + 32, hi); ++t, ++cnt) {
+                    // strips of different slices (and K ranges) are different data
+                    const int64_t zz = t / per;
+                    ms[cnt] = zz * tiles_m + tile_of(t % per, g, tiles_m, tiles_n, &ns[cnt]);
+                    ns[cnt] += zz * tiles_n;
+                }
+                std::sort(ms, ms + cnt);
+                std::sort(ns, ns + cnt);
+                const int64_t dm = std::unique(ms, ms + cnt) - ms, dn = std::unique(ns, ns + cnt) - ns;
+                bytes += (double)dm * a_strip + (double)dn * b_strip;
+            }
+        }
+        if (first || bytes < best_bytes * (1.0 - 1e-9)) {
+            best = g;
+            best_bytes = bytes;
+        }
+        first = false;
+    }
+    return (int)std::min<int64_t>(best, 127);
 }
 
 hipError_t launch_tiled(const Problem &p, const Launch &l, hipStream_t s) {
     int tiles_m = (int)((p.M + l.tile_m - 1) / l.tile_m);
     int tiles_n = (int)((p.N + l.tile_n - 1) / l.tile_n);
-    int n_fast = l.order;
+    int group_m = l.group_m;
     Problem pp = p;
-    void *args[] = {&pp, &tiles_m, &tiles_n, &n_fast};
+    void *args[] = {&pp, &tiles_m, &tiles_n, &group_m};
     const void *fn = nullptr;
     switch (p.a_type) {
     case OUTPROD_TYPE_F32: fn = tiled_kernel_f32(p.a_type, l.variant, p.b_kt); break;

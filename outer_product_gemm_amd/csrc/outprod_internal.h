@@ -58,8 +58,9 @@ struct Launch {
     int64_t grid;     // main kernel workgroups (all splits)
     int splits;       // 1 = no split
     int64_t ksplit;   // rows per split
-    int order;        // tiled kernel: 0 = tiles walk i0 fastest within a slice,
-                      // 1 = i1 fastest; on entry to plan_tiled, -1 = automatic
+    int group_m;      // tiled kernel: tiles walk groups of group_m m-tiles within
+                      // a slice (i0 fastest inside a group); on entry to
+                      // plan_tiled, 0 = automatic
 };
 
 // A validated OUT_PROD call and its plan.  swapped: the problem runs with
@@ -112,7 +113,7 @@ hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s);
 // Per-kernel planning (host only, no HIP calls) and launching.
 bool plan_skinny(const Problem &p, Launch *l);
 bool plan_tiled(const Problem &p, Launch *l);
-int tile_order_n_fast(const Problem &p, const Launch &l, int64_t tiles_m, int64_t tiles_n);
+int tile_group_m(const Problem &p, const Launch &l, int64_t tiles_m, int64_t tiles_n);
 void plan_zero(const Problem &p, Launch *l);
 
 hipError_t launch_skinny(const Problem &p, const Launch &l, hipStream_t s);

@@ -877,7 +877,7 @@ struct TileCore {
 
 template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
 __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int tiles_m,
-                                                               int tiles_n, int n_fast) {
+                                                               int tiles_n, int group_m) {
     typedef TileCore<MF, FM, FN, WGM, WGN, BK> C;
     constexpr int T = C::T, BM = C::BM, BN = C::BN;
     __shared__ __attribute__((aligned(16))) float As[2][BK][C::LDA];
@@ -891,10 +891,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     const int slices = (int)(p0.ne12 * p0.ne13);
     const int zz = logical / per_slice, rem = logical % per_slice;
     const int z = zz % slices, sp = zz / slices;
-    // n_fast: consecutive logical tiles walk i1 (they share a's strip)
-    // instead of i0 (sharing b's strip)
-    const int m0 = (n_fast ? rem / tiles_n : rem % tiles_m) * BM;
-    const int n0 = (n_fast ? rem % tiles_n : rem / tiles_m) * BN;
+    // consecutive logical tiles walk groups of group_m m-tiles, i0 fastest
+    // within a group (group_m = tiles_m: i0 fastest over the slice; 1: i1
+    // fastest); the last group may be narrower
+    const int gsize = group_m * tiles_n;
+    const int grp = rem / gsize, idx = rem % gsize;
+    const int gm = tiles_m - grp * group_m < group_m ? tiles_m - grp * group_m : group_m;
+    const int m0 = (grp * group_m + idx % gm) * BM;
+    const int n0 = (idx / gm) * BN;
     Problem p = p0;
     SliceBase s = slice_base(p, z);
     if (p.splits > 1) apply_split(p, s, z, sp);

@@ -172,10 +172,10 @@ def test_forced_kernels():
     p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.KERNEL_SKINNY)
     assert p["kernel_name"] == "skinny" and p["tile_m"] == 32 and p["tile_n"] == 32 and p["grid"] == 2 * 80
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=7)] == "E_KERNEL"
-    for cfg in range(11):
+    for cfg in range(13):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_SKINNY, cfg))
         assert p["kernel_name"] == "skinny" and p["variant"] == cfg
-    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 11))] == "E_KERNEL"
+    assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 13))] == "E_KERNEL"
     # every tiled configuration can be forced; an unknown one is refused
     for cfg in range(15):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
@@ -355,25 +355,26 @@ def test_id_back_every_type_plans(a_type):
 
 
 def test_tile_order_reported_and_forced():
-    """The tiled kernel's tile order within a slice (i0 or i1 fastest) is
-    reported by the plan, chosen per shape (i1 fastest for the tall m17408
-    q4_K weight, i0 fastest at m5120) and can be forced either way; other
-    families refuse an order and report -1."""
-    for name, want in (("q4_K_5120x17408", 0), ("q4_K_17408x5120", 1)):
+    """The tiled kernel's tile order within a slice (groups of group_m tiles
+    along i0, i0 fastest inside a group) is reported by the plan and chosen
+    per shape: i0 fastest for m5120 k17408 (one round of tiles per XCD, every
+    XCD's tiles share one b strip), groups of 8 for m17408 k5120 (two rounds:
+    8 a strips and 4 b strips per round).  It can be forced (a value past the
+    tiles along i0 means i0 fastest); other families refuse it and report 0."""
+    for name, want in (("q4_K_5120x17408", 64), ("q4_K_17408x5120", 8)):
         a_type, a_ne, b_ne = synth.WORKLOADS[name][:3]
         ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne)
         p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
-        assert p["kernel_name"] == "tiled" and p["tile_order"] == want, (name, p)
-        for order in (0, 1):
-            code = B.kernel_code(B.KERNEL_TILED, p["variant"], None, order)
+        assert p["kernel_name"] == "tiled" and p["group_m"] == want, (name, p)
+        tiles_m = -(-a_ne[0] // p["tile_m"])
+        for g, expect in ((1, 1), (3, 3), (127, min(127, tiles_m))):
+            code = B.kernel_code(B.KERNEL_TILED, p["variant"], None, g)
             q = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb, code)
-            assert q["tile_order"] == order and q["variant"] == p["variant"] and q["grid"] == p["grid"]
-        bad = B.kernel_code(B.KERNEL_TILED) | (3 << 24)
-        assert B.STATUS[B.plan_status(A, a_type, 0x40000000000, 0x80000000000, ne, nb, bad)] == "E_KERNEL"
+            assert q["group_m"] == expect and q["variant"] == p["variant"] and q["grid"] == p["grid"]
     ne, nb = base()
-    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["tile_order"] == -1
+    assert B.out_prod_plan(A, synth.F32, BB, D, ne, nb)["group_m"] == 0
     for fam in (B.KERNEL_SKINNY, B.KERNEL_AUTO):
-        code = B.kernel_code(fam, None, None, 0)
+        code = B.kernel_code(fam, None, None, 2)
         assert B.STATUS[plan(synth.F32, ne, nb, kernel=code)] == "E_KERNEL"
 
 

@@ -94,7 +94,7 @@ def test_every_tiled_configuration(cfg):
         check_case(inst, code)
 
 
-@pytest.mark.parametrize("cfg", range(11))
+@pytest.mark.parametrize("cfg", range(13))
 def test_every_column_configuration(cfg):
     """Each column-kernel configuration, forced, on ragged f32 shapes (partial
     column strips, i0 blocks, K not a multiple of the wave steps, a column
@@ -102,7 +102,8 @@ def test_every_column_configuration(cfg):
     that vector loads are off)."""
     code = B.kernel_code(B.KERNEL_SKINNY, cfg)
     for a_ne, b_ne in (((8, 517, 1, 1), (333, 517, 1, 1)), ((24, 130, 2, 1), (70, 130, 4, 1)),
-                       ((50, 77, 1, 1), (45, 77, 1, 1)), ((3, 1100, 1, 1), (1030, 1100, 1, 1))):
+                       ((50, 77, 1, 1), (45, 77, 1, 1)), ((3, 1100, 1, 1), (1030, 1100, 1, 1)),
+                       ((24, 512, 1, 1), (640, 512, 1, 1)), ((30, 520, 1, 1), (96, 520, 1, 1))):
         inst = synth.make_instance("col%d" % cfg, synth.F32, a_ne, b_ne, seed_of(cfg, a_ne))
         check_case(inst, code)
     inst = synth.make_instance("colmis%d" % cfg, synth.F32, (8, 300, 1, 1), (200, 300, 1, 1), cfg)

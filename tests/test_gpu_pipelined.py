@@ -85,12 +85,11 @@ def test_full_tiles_every_stage_count(cfg):
 
 
 @pytest.mark.parametrize("cfg", [8, 9, 14, 0, 4])
-def test_tile_order_both_ways(cfg):
-    """Both tile orders (i0 or i1 fastest within a slice), forced through
-    out_prod_ex and confirmed by the plan, on grids with broadcast slices,
-    full and ragged tiles, for q4_K and f32 a; the automatic choice takes
-    each order on some of these shapes."""
-    auto_orders = set()
+def test_tile_order_every_way(cfg):
+    """Tile orders forced through out_prod_ex and confirmed by the plan --
+    i1 fastest (groups of 1), groups of 3 (a narrower last group when the
+    tiles along i0 are not a multiple of 3), i0 fastest (127) -- on grids with
+    broadcast slices, full and ragged tiles, for q4_K and f32 a."""
     for a_type, M, N, dps2 in ((synth.Q4_K, 4352, 256, 2), (synth.Q4_K, 512, 1100, 2),
                                (synth.F32, 4400, 130, 3), (synth.F32, 300, 900, 1),
                                (synth.Q4_K, 8192, 512, 2)):
@@ -102,17 +101,17 @@ def test_tile_order_both_ways(cfg):
         d_d = torch.empty(G.dst_extent_floats(inst.ne, inst.nb), dtype=torch.float32, device="cuda:0")
         auto = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne,
                                inst.nb, B.kernel_code(B.KERNEL_TILED, cfg))
-        auto_orders.add(auto["tile_order"])
+        tiles_m = -(-M // auto["tile_m"])
+        assert 1 <= auto["group_m"] <= tiles_m
         ref, den = oracle.out_prod(inst.a, inst.a_type, inst.b, inst.ne, inst.nb)
-        for order in (0, 1):
-            code = B.kernel_code(B.KERNEL_TILED, cfg, None, order)
+        for g in (1, 3, 127):
+            code = B.kernel_code(B.KERNEL_TILED, cfg, None, g)
             plan = B.out_prod_plan(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), d_d.data_ptr(), inst.ne,
                                    inst.nb, code)
-            assert plan["tile_order"] == order
-            G.log("case order cfg", cfg, synth.TYPE_NAMES[a_type], M, N, dps2, "order", order,
-                  "auto", auto["tile_order"])
+            assert plan["group_m"] == min(g, tiles_m)
+            G.log("case order cfg", cfg, synth.TYPE_NAMES[a_type], M, N, dps2, "group_m",
+                  plan["group_m"], "tiles_m", tiles_m, "auto", auto["group_m"])
             gpu = G.run(inst.a, inst.a_type, inst.b, inst.ne, inst.nb, code)
             res = oracle.check(gpu, ref, den, TOL)
             assert np.isfinite(gpu).all()
-            assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], M, N, order, res)
-    assert auto_orders == {0, 1}, auto_orders
+            assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], M, N, g, res)
