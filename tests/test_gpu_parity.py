@@ -310,7 +310,9 @@ def test_tensor_helper_matches_raw_call():
 def test_graph_capture_replays_match_eager():
     """Launches captured in a HIP graph: every replay, with eager work on the
     same buffers between replays, equals the eager result (b scaled by 2 in
-    place between replays scales dst by exactly 2)."""
+    place between replays scales dst by exactly 2).  One uncaptured call on
+    the capture stream first binds its workspace, so a plan that splits K
+    (the rank-8 gradient) keeps its split under capture."""
     for name in ("lora_r8_single", "deltanet_bcast", "q8_0_5120"):
         inst = synth.workload(name)
         a_d = G.to_dev(np.ascontiguousarray(inst.a).view(np.uint8).reshape(-1))
@@ -324,6 +326,9 @@ def test_graph_capture_replays_match_eager():
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
+        B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb,
+                   cap.cuda_stream)
+        torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=cap):
             B.out_prod(a_d.data_ptr(), inst.a_type, b_d.data_ptr(), out.data_ptr(), inst.ne, inst.nb,
                        torch.cuda.current_stream().cuda_stream)
@@ -338,6 +343,9 @@ def test_graph_capture_replays_match_eager():
             assert np.array_equal(got, ref * np.float32(scale)), (name, rep)
             b_d.mul_(2.0)          # eager work on the captured buffer
             scale *= 2.0
+        del g
+        torch.cuda.synchronize()
+        B.out_prod_release_stream(cap.cuda_stream)
 
 
 # ---------------------------------------------------------------- b as a transposed view

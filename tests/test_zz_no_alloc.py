@@ -47,7 +47,7 @@ def test_noalloc_matches_out_prod_on_consecutive_calls():
     assert torch.cuda.is_available()
     B.load_library()
     stream = torch.cuda.current_stream().cuda_stream
-    big, small, plain = Dev("lora4B_dxW"), Dev("lora4B_dh"), Dev("lora_r8_2560")
+    big, small, plain = Dev("lora4B_dxW"), Dev("lora4B_dh"), Dev("deltanet_bcast")
     assert big.plan["splits"] > 1 and small.plan["splits"] > 1 and plain.plan["splits"] == 1
     assert small.plan["workspace_bytes"] < big.plan["workspace_bytes"] <= SCRATCH_BYTES
     refs = []
@@ -69,14 +69,8 @@ def test_noalloc_matches_out_prod_on_consecutive_calls():
             assert np.array_equal(got, ref), (d.inst.name, rep)
             if rep == 0:
                 i = d.inst
-                cols = None if i.ne[4] <= 1024 else np.arange(0, i.ne[4], 37)
-                if cols is None:
-                    r, den = oracle.out_prod(i.a, i.a_type, i.b, i.ne, i.nb)
-                    res = oracle.check(got, r, den, 1e-5)
-                else:
-                    sel = np.array([[c, 0, 0] for c in cols])
-                    r, den = oracle.out_prod(i.a, i.a_type, i.b, i.ne, i.nb, cols=sel)
-                    res = oracle.check(got[0, 0, cols], r, den, 1e-5)
+                r, den = oracle.out_prod(i.a, i.a_type, i.b, i.ne, i.nb)
+                res = oracle.check(got, r, den, 1e-5)
                 assert res["ok"], (d.inst.name, res)
     assert B.out_prod_workspace_count() == n_ws
     # (the HIP runtime may map a few MiB of its own on first use of a path)
