@@ -42,6 +42,8 @@ RIDGE = PEAK_MFMA_F32_TFLOPS * 1e3 / PEAK_HBM_GBPS   # flop per byte
 
 COMPOSITE = {
     "q4_K_27B_both": ["q4_K_5120x17408", "q4_K_17408x5120"],
+    # all four of the pages' per-op q4_K training shapes (n = 1024)
+    "q4_K_page_shapes": ["q4_K_1536x1536", "q4_K_5120x5120", "q4_K_5120x17408", "q4_K_17408x5120"],
 }
 # The five OUT_PRODs of one LoRA-adapted linear layer's backward (frozen q4_K
 # weight, rank 8): input gradient through W and through A, the gradient of
@@ -60,9 +62,10 @@ DEFAULT_WORKLOAD = "q4_K_27B_both"
 
 # The pages' per-op float-staging times for the same q4_K x f32 shapes
 # (Apple M5, Metal; "metal: OUT_PROD multiplies in float staging", review
-# answer on cost): midpoints of 88-94 ms and 88-90 ms.  Another machine:
-# context for vs_baseline only.
-PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0}
+# answer on cost): midpoints of 88-94, 88-90, 2.8-2.9 and 26-27 ms.  Another
+# machine: context for vs_baseline only.
+PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0, "q4_K_1536x1536": 2.85,
+           "q4_K_5120x5120": 26.5}
 
 # HBM traffic per launch from rocprofv3 PMC runs (FETCH_SIZE + WRITE_SIZE,
 # scaled by the copy-kernel calibration), keyed by workload, valid only for

@@ -17,8 +17,11 @@
 //   3. id_place_kernel  the expert-sorted slot list; a slot whose id is not
 //      an expert gets a NaN dst row;
 //   4. tiled_id_kernel  (tiled_impl.h) one workgroup per (tile, m-tile).
-// Slots keep their order within an expert, every dst row has one writer and
-// its sum runs over K in a fixed order: the result is deterministic.  The
+// Up to kIdRouteFused slots, one block does 1-3 in a single launch
+// (id_route_kernel), ranking the slots within their experts with LDS
+// atomics; the three kernels keep the slots' order within an expert.
+// Every dst row has one writer and its sum runs over K in a fixed order
+// whatever tile holds its slot: the result is deterministic.  The
 // tables live in the stream's workspace; nothing is cleared in advance (every
 // entry read is written first, in stream order).
 #include <algorithm>
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(kIdRankBlock) void id_rank_kernel(IdProblem p) {
     unsigned long long todo = __ballot(e >= 0);
     while (todo) {
         const int leader = __ffsll((unsigned long long)todo) - 1;
-        const int le = __shfl(e, leader);
+        const int le = __builtin_amdgcn_readlane(e, leader);
         const unsigned long long peers = __ballot(e == le);
         if (e == le) rank = __popcll(peers & ((1ull << lane) - 1ull));
         if (lane == leader) wcnt[wave][le] = __popcll(peers);
@@ -135,6 +138,79 @@ __global__ __launch_bounds__(256) void id_place_kernel(IdProblem p) {
     ws[p.off_sorted + pos] = s;
 }
 
+// Steps 1-3 in one block of 1024 threads for at most kIdRouteFused slots:
+// the same per-expert offsets and tile table as the three kernels, and a
+// sorted list that holds each expert's slots in an order set by LDS atomics
+// (which tile a slot lands in changes no value: a dst row's sum depends
+// only on its own gradient column and the expert).  Thread t holds slots
+// t, t + 1024, ... in registers, their ids loaded at once.
+__global__ __launch_bounds__(1024) void id_route_kernel(IdProblem p) {
+    constexpr int R = kIdRouteFused / 1024;
+    __shared__ int cnt[kIdMaxExperts];  // slots per expert, then the expert's offset
+    __shared__ int sc[1024], st[1024];
+    const int tid = threadIdx.x;
+    const int E = (int)p.n_expert, nu = (int)p.n_used;
+    const int total = (int)(p.n_used * p.n_tokens);
+    int *ws = (int *)p.ws;
+    int ev[R], rk[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = r * 1024 + tid;
+        ev[r] = -1;
+        if (s < total) {
+            const int i = s % nu, t = s / nu;
+            const int v = *(const int *)(p.ids + (int64_t)i * 4 + (int64_t)t * p.nbi1);
+            ev[r] = (v >= 0 && v < E) ? v : -1;
+        }
+    }
+    for (int x = tid; x < E; x += 1024) cnt[x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) rk[r] = ev[r] >= 0 ? atomicAdd(&cnt[ev[r]], 1) : -1;
+    __syncthreads();
+    // per-expert offsets and the tile table (as id_scan_kernel)
+    const int c = tid < E ? cnt[tid] : 0;
+    const int nt = (c + p.bn - 1) / p.bn;
+    sc[tid] = c;
+    st[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < E; off <<= 1) {
+        const int a = tid >= off ? sc[tid - off] : 0;
+        const int b = tid >= off ? st[tid - off] : 0;
+        __syncthreads();
+        sc[tid] += a;
+        st[tid] += b;
+        __syncthreads();
+    }
+    if (tid < E) {
+        cnt[tid] = sc[tid] - c;
+        ws[p.off_offsets + tid] = sc[tid] - c;
+        const int t0 = st[tid] - nt;
+        for (int j = 0; j < nt; ++j) {
+            ws[p.off_tile_e + t0 + j] = tid;
+            ws[p.off_tile_r0 + t0 + j] = j * p.bn;
+        }
+    }
+    if (tid == E - 1) {
+        ws[p.off_offsets + E] = sc[tid];
+        ws[p.off_ntiles] = st[tid];
+    }
+    __syncthreads();
+    // the sorted list (as id_place_kernel)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = r * 1024 + tid;
+        if (s >= total) continue;
+        if (rk[r] >= 0) {
+            ws[p.off_sorted + cnt[ev[r]] + rk[r]] = s;
+        } else {  // id outside [0, n_expert): the row is NaN
+            const int i = s % nu, t = s / nu;
+            float *d = (float *)(p.dst + (int64_t)i * p.nbd1 + (int64_t)t * p.nbd2);
+            for (int m = 0; m < (int)p.M; ++m) d[m] = __builtin_nanf("");
+        }
+    }
+}
+
 const void *id_kernel_for(int a_type, int cfg) {
     using namespace tiled;
     switch (a_type) {
@@ -192,26 +268,28 @@ double expected_tiles_per_expert(const IdProblem &p, int bn) {
 }
 
 // Grouped-kernel configurations the automatic choice considers: 64 x 64,
-// 128 x 80 and 128 x 128 tiles (the others can be forced), with their rates
-// in the grouped kernel (TileCfg::eff's unit).  The rates come from
+// 128 x 80 and 128 x 128 tiles of 4 waves and 128 x 128 tiles of 8 waves
+// whose waves each span the 128 slots (the others can be forced), with their
+// rates in the grouped kernel (TileCfg::eff's unit).  The rates come from
 // graph-timed launches of each configuration, forced, on 64 q4_K experts, 8
-// of 64 routed, 512 tokens (ne00 2560 x K 1024: 323 / 334 / 403 us for
-// 64 x 64 / 128 x 80 / 128 x 128; ne00 1024 x K 2560: 357 / 407 / 439 us),
-// divided into the work the cost model below counts for each; partly filled
-// tiles and the gathered slot columns make the wider slot tiles relatively
-// slower here than in a dense OUT_PROD.
+// of 64 routed, 512 tokens (ne00 2560 x K 1024: 323 / 334 / 403 / 322 us;
+// ne00 1024 x K 2560: 357 / 407 / 439 / 322 us, routing included), divided
+// into the work the cost model below counts for each; partly filled tiles
+// and the gathered slot columns make the wider slot tiles relatively slower
+// here than in a dense OUT_PROD, except where every wave skips the same
+// empty blocks.
 struct IdAutoCfg {
     int cfg;
     double eff;
 };
-constexpr IdAutoCfg kIdAuto[] = {{4, 10.6}, {12, 8.35}, {0, 11.45}};
+constexpr IdAutoCfg kIdAuto[] = {{4, 10.6}, {12, 8.35}, {0, 11.45}, {15, 14.5}};
 
 // l->variant on entry: forced configuration + 1 (an index into kCfgs that is
 // built for the grouped kernel), or 0 for automatic.  The automatic choice
 // minimizes the estimated time: workgroups x tile area x K / eff, slowed in
-// proportion when there are fewer than 640 workgroups (2.5 per CU: the CUs'
-// MFMA pipes are not kept busy), with the workgroup count from the expected
-// tiles per expert.  Both shapes above run best with 64 x 64 tiles.
+// proportion when there are fewer than 2560 waves (10 per CU: the CUs' MFMA
+// pipes are not kept busy), with the workgroup count from the expected tiles
+// per expert.  The shapes above run best with the 8-wave 128 x 128 tiles.
 bool plan_id_back(IdProblem &p, Launch *l) {
     using namespace tiled;
     int best = -1;
@@ -225,7 +303,7 @@ bool plan_id_back(IdProblem &p, Launch *l) {
             const TileCfg &c = kCfgs[a.cfg];
             const double wgs = (double)((p.M + c.bm() - 1) / c.bm()) * (double)p.n_expert *
                                expected_tiles_per_expert(p, c.bn());
-            const double fill = std::min(1.0, wgs / 640.0);
+            const double fill = std::min(1.0, wgs * (c.threads() / 64) / 2560.0);
             const double cost = wgs * c.bm() * c.bn() * (double)p.K / a.eff / fill;
             if (best < 0 || cost < best_cost) {
                 best = a.cfg;
@@ -254,13 +332,18 @@ hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s) {
     IdProblem pp = p;
     const int64_t slots = p.n_used * p.n_tokens;
     void *args1[] = {&pp};
-    hipError_t e = hipLaunchKernel((const void *)&id_rank_kernel, dim3((unsigned)p.rank_blocks),
-                                   dim3(kIdRankBlock), args1, 0, s);
-    if (e == hipSuccess)
-        e = hipLaunchKernel((const void *)&id_scan_kernel, dim3(1), dim3(1024), args1, 0, s);
-    if (e == hipSuccess)
-        e = hipLaunchKernel((const void *)&id_place_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256),
+    hipError_t e;
+    if (slots <= kIdRouteFused) {
+        e = hipLaunchKernel((const void *)&id_route_kernel, dim3(1), dim3(1024), args1, 0, s);
+    } else {
+        e = hipLaunchKernel((const void *)&id_rank_kernel, dim3((unsigned)p.rank_blocks), dim3(kIdRankBlock),
                             args1, 0, s);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void *)&id_scan_kernel, dim3(1), dim3(1024), args1, 0, s);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void *)&id_place_kernel, dim3((unsigned)((slots + 255) / 256)),
+                                dim3(256), args1, 0, s);
+    }
     if (e != hipSuccess) return e;
     int tiles_m = (int)((p.M + l.tile_m - 1) / l.tile_m);
     void *args[] = {&pp, &tiles_m};

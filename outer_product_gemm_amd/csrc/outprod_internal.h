@@ -105,6 +105,7 @@ struct IdProblem {
 // Limits of MUL_MAT_ID_BACK: experts per op (the rank kernel's LDS tables).
 constexpr int kIdMaxExperts = 512;
 constexpr int kIdRankBlock = 1024;  // slots per rank-kernel block (16 waves)
+constexpr int kIdRouteFused = 16384;  // most slots routed by the one-block kernel
 
 bool plan_id_back(IdProblem &p, Launch *l);   // sets the tile config and table layout
 int64_t id_workspace_bytes(const IdProblem &p);

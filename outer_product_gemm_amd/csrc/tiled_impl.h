@@ -1002,7 +1002,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, i
     // waves whose slot rows are all past the expert's last slot skip their MFMAs
     typename C::acc_t acc[FM][FN];
     // MFMA blocks of MF slot rows this wave needs: those holding a slot
-    const int wave_row0 = (int)(threadIdx.x >> 6) / WGM * C::WTN;  // the wave's first slot row
+    const int wave_row0 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / WGM * C::WTN;  // first slot row
     const int need = (cnt - wave_row0 + MF - 1) / MF;
     const int fn_act = need < 0 ? 0 : need > FN ? FN : need;
     const bool a_vec_ok = (AT != OUTPROD_TYPE_F32 && AT != OUTPROD_TYPE_F16 && AT != OUTPROD_TYPE_BF16) ||
@@ -1057,6 +1057,13 @@ struct TileCfg {
 // 14: 80 x 256, 8 waves of 80 x 32 (16x16x4) in one row, 32-row stages --
 //     m5120 x n1024 in 256 tiles with half the a decode per flop of 8 (the
 //     planner rates it per a type: cfg_eff)
+// Grouped MUL_MAT_ID_BACK only (past kNumCfgs): 128-slot tiles that every
+// wave spans whole, so in a tile holding an expert's few dozen slots every
+// wave skips the same MFMA blocks:
+// 15: 128 x 128, 8 waves of 16 x 128 (16x16x4)
+// 16: 128 x 128, 4 waves of 32 x 128 (16x16x4)
+// (64 x 128 tiles of 4 waves and 32-row stages of 15 ran at half its rate
+// on the 64-expert shapes below.)
 constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 16, 12.4f},
     {16, 5, 2, 2, 4, 16, 11.5f},
@@ -1073,8 +1080,11 @@ constexpr TileCfg kCfgs[] = {
     {16, 2, 5, 4, 1, 16, 10.4f},
     {16, 1, 5, 4, 1, 16, 10.0f},
     {16, 5, 2, 1, 8, 32, 12.5f},
+    {16, 1, 8, 8, 1, 16, 10.0f},
+    {16, 2, 8, 4, 1, 16, 10.0f},
 };
-constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+// The OUT_PROD menu: configurations 0 .. kNumCfgs-1.
+constexpr int kNumCfgs = 15;
 
 template <int AT, int C, bool BT>
 const void *cfg_fn() {
@@ -1110,7 +1120,7 @@ const void *tiled_fn(int variant, bool bt) {
 
 // Tile configurations the grouped MUL_MAT_ID_BACK kernel is built for
 // (indices into kCfgs): 64-, 80- and 128-slot tiles, 16- and 32-row stages.
-constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13};
+constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13, 15, 16};
 constexpr int kNumIdCfgs = sizeof(kIdCfgs) / sizeof(kIdCfgs[0]);
 
 template <int AT, int C>
@@ -1131,6 +1141,8 @@ const void *id_fn(int cfg) {
     case 11: return id_cfg_fn<AT, 11>();
     case 12: return id_cfg_fn<AT, 12>();
     case 13: return id_cfg_fn<AT, 13>();
+    case 15: return id_cfg_fn<AT, 15>();
+    case 16: return id_cfg_fn<AT, 16>();
     default: return nullptr;
     }
 }

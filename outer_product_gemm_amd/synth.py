@@ -246,6 +246,11 @@ WORKLOADS = {
                         "27B q4_K weight x f32 gradient, m 5120 k 17408 n 1024"),
     "q4_K_17408x5120": (Q4_K, (17408, 5120, 1, 1), (1024, 5120, 1, 1), 52, 1.0, "normal",
                         "27B q4_K weight x f32 gradient, m 17408 k 5120 n 1024"),
+    # the pages' two smaller per-op q4_K training shapes (n = 1024)
+    "q4_K_1536x1536": (Q4_K, (1536, 1536, 1, 1), (1024, 1536, 1, 1), 53, 1.0, "normal",
+                       "q4_K weight x f32 gradient, m 1536 k 1536 n 1024"),
+    "q4_K_5120x5120": (Q4_K, (5120, 5120, 1, 1), (1024, 5120, 1, 1), 54, 1.0, "normal",
+                       "q4_K weight x f32 gradient, m 5120 k 5120 n 1024"),
 }
 
 

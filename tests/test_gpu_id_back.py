@@ -4,6 +4,7 @@ Gate as for OUT_PROD: no NaN/Inf except where an id is not an expert (that row
 must be all NaN), |gpu - ref| <= 1e-5 * sum_r |a||g| per element.  Routing is
 seeded: distinct top-k experts per token, plus skewed and invalid routings.
 """
+import dataclasses
 import zlib
 
 import numpy as np
@@ -96,9 +97,32 @@ def test_id_back_every_type(a_type):
     check_id(inst, gpu)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 8, 10, 11, 12, 13])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16])
 def test_id_back_every_configuration(cfg):
     inst = synth.make_moe_instance("c", synth.Q4_K, 768, 130, 9, 4, 150, seed_of("idc", cfg))
+    gpu, _ = run_id(inst, kernel=B.kernel_code(B.KERNEL_TILED, cfg))
+    check_id(inst, gpu)
+
+
+@pytest.mark.parametrize("a_type", ALL_TYPES)
+def test_id_back_whole_stages_every_type(a_type):
+    """K a whole number of 32-row stages and ne00 = 512 (whole m-tiles for
+    most tile heights), partly filled slot tiles."""
+    inst = synth.make_moe_instance("tp", a_type, 512, 128, 6, 3, 70, seed_of("idtp", a_type))
+    G.log("case id_back whole stages", synth.TYPE_NAMES[a_type], inst.ne[:3], "slots", 210)
+    gpu, _ = run_id(inst)
+    check_id(inst, gpu)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16])
+@pytest.mark.parametrize("shape", [(768, 160, 9, 4, 150), (1024, 256, 5, 4, 150)])
+def test_id_back_whole_stages_every_configuration(cfg, shape):
+    """Whole stages and aligned columns (and, where 768 is not a multiple of
+    the tile height, a ragged last m-tile); 5 experts of 120 slots on average
+    give full slot tiles (the unchecked loop) next to partly filled ones."""
+    ne00, K, n_e, n_u, n_t = shape
+    inst = synth.make_moe_instance("cp", synth.Q4_K, ne00, K, n_e, n_u, n_t, seed_of("idcp", cfg, ne00))
+    G.log("case id_back whole stages cfg", cfg, inst.ne[:3])
     gpu, _ = run_id(inst, kernel=B.kernel_code(B.KERNEL_TILED, cfg))
     check_id(inst, gpu)
 
@@ -115,6 +139,30 @@ def test_id_back_skewed_routing_and_repeat():
     inst.ids[:] = np.where(np.arange(600)[:, None] % 3 == 0, 11, 2).astype(np.int32)
     gpu, _ = run_id(inst)
     check_id(inst, gpu)
+
+
+def test_id_back_routing_paths_agree():
+    """18000 slots (past the one-block routing kernel's 16384: the three
+    routing kernels), with three invalid ids, against the oracle; the first
+    2000 tokens alone (12000 slots, one-block routing) give bit-identical
+    rows."""
+    inst = synth.make_moe_instance("many", synth.Q8_0, 64, 32, 40, 6, 3000, seed_of("many"))
+    ids = inst.ids.copy()
+    bad = [(5, 2, 40), (1999, 0, -3), (2999, 5, 1 << 30)]
+    for t, i, v in bad:
+        ids[t, i] = v
+    gpu, _ = run_id(inst, ids=ids)
+    valid = np.ones((3000, 6), dtype=bool)
+    for t, i, _ in bad:
+        valid[t, i] = False
+        assert np.isnan(gpu[t, i]).all()
+    slots = [t * 6 + i for t in range(3000) for i in range(6) if valid[t, i]]
+    ref = dataclasses.replace(inst, ids=np.where(valid, ids, 0).astype(np.int32))
+    check_id(ref, gpu, slots=slots)         # oracle: the valid slots only
+    ne = list(inst.ne)
+    ne[6] = ne[9] = ne[14] = 2000           # g, ids and dst over the first 2000 tokens
+    small, _ = run_id(dataclasses.replace(inst, ne=ne), ids=ids)
+    assert np.array_equal(small.view(np.uint32), gpu[:2000].view(np.uint32))
 
 
 def test_id_back_invalid_ids_give_nan_rows():

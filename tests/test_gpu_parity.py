@@ -123,7 +123,7 @@ def test_rank1_K1_bit_exact():
 
 # The benchmarked q8_0 and q4_K launches: their whole output is checked
 # (the oracle needs a few seconds per launch on the host's cores).
-WHOLE_OUTPUT = ("q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120")
+WHOLE_OUTPUT = ("q8_0_5120", "q4_K_5120x17408", "q4_K_17408x5120", "q4_K_5120x5120")
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
