@@ -33,13 +33,16 @@ double cfg_eff(int cfg, int a_type) {
 }
 
 // Estimated time (us) of a configuration with `splits` K ranges: the
-// busiest CU runs ceil(tiles * splits / 256) tiles of ksplit rows each at
-// the configuration's efficiency, plus the split's reduction.
+// busiest CU runs ceil(tiles * splits / 256) tiles of ksplit rows each --
+// rounded up to whole stages, whose padding rows cost as much as real ones
+// -- at the configuration's efficiency, plus the split's reduction.
 double cfg_cost(int cfg, const Problem &p, int splits, int64_t ksplit) {
     const TileCfg &c = kCfgs[cfg];
     const int64_t tiles = ((p.M + c.bm() - 1) / c.bm()) * ((p.N + c.bn() - 1) / c.bn()) * p.ne12 * p.ne13;
     const int64_t per_cu = (tiles * splits + 255) / 256;
-    double t = (double)per_cu * c.bm() * c.bn() * (double)ksplit / cfg_eff(cfg, p.a_type) / kEffPerUs;
+    const int64_t krows = ksplit < p.K ? ksplit : p.K;
+    const int64_t kpad = (krows + c.bk - 1) / c.bk * c.bk;
+    double t = (double)per_cu * c.bm() * c.bn() * (double)kpad / cfg_eff(cfg, p.a_type) / kEffPerUs;
     if (splits > 1)
         t += kSplitLaunchUs + (double)(2 * splits) * p.M * p.N * p.ne12 * p.ne13 * 4 / kSplitBytesPerUs;
     return t;

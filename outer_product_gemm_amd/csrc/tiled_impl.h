@@ -1076,7 +1076,7 @@ constexpr TileCfg kCfgs[] = {
     {16, 5, 2, 2, 4, 32, 12.2f},
     {16, 17, 1, 1, 8, 32, 12.1f},
     {16, 5, 2, 2, 2, 32, 10.3f},
-    {32, 1, 1, 2, 2, 32, 10.5f},
+    {32, 1, 1, 2, 2, 32, 10.7f},
     {16, 2, 5, 4, 1, 16, 10.4f},
     {16, 1, 5, 4, 1, 16, 10.0f},
     {16, 5, 2, 1, 8, 32, 12.5f},
