@@ -660,7 +660,11 @@ struct TileCore {
     // PART, a wave runs only its first fn_act (wave-uniform) MFMA blocks along
     // the tile's rows: the rows past them are not needed (a grouped tile
     // holding fewer slots than its height), so those MFMAs are skipped.
-    template <bool FULL, bool PART = false, class LA, class LB>
+    // With DEEP, two register sets of raw operand data: a stage's global
+    // loads are issued two stages before its decode into LDS (one stage
+    // without), for tiles with too little MFMA work per stage to cover a
+    // load's latency in one.
+    template <bool FULL, bool PART = false, bool DEEP = false, class LA, class LB>
     __device__ static void run(LA &la, LB &lb, int K, float (&As)[2][BK][LDA],
                                float (&Bs)[2][BK][LDB], acc_t (&acc)[FM][FN], int fn_act = FN) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -673,13 +677,19 @@ struct TileCore {
                 for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
 
         const int ktiles = (K + BK - 1) / BK;
+        LA la1 = la;  // DEEP: the second register set (odd stages)
+        LB lb1 = lb;
         la.template load<FULL>(0);
         lb.template load<FULL>(0);
+        if (DEEP && ktiles > 1) {
+            la1.template load<FULL>(BK);
+            lb1.template load<FULL>(BK);
+        }
         la.store(As[0]);
         lb.store(Bs[0]);
-        if (ktiles > 1) {
-            la.template load<FULL>(BK);
-            lb.template load<FULL>(BK);
+        if (ktiles > 1 + DEEP) {
+            la.template load<FULL>((1 + DEEP) * BK);
+            lb.template load<FULL>((1 + DEEP) * BK);
         }
         __syncthreads();
 
@@ -722,21 +732,45 @@ struct TileCore {
         };
         const bool mma = !PART || fn_act > 0;
 
-        for (int t = 0; t < ktiles; ++t) {
-            const int cur = t & 1;
-            if (mma) mfma_steps(cur, 0, S / 2);
-            if (t + 1 < ktiles) {
-                // registers hold stage t+1: decode into the free buffer, then
-                // start stage t+2's loads
-                la.store(As[cur ^ 1]);
-                lb.store(Bs[cur ^ 1]);
-                if (t + 2 < ktiles) {
-                    la.template load<FULL>((t + 2) * BK);
-                    lb.template load<FULL>((t + 2) * BK);
+        if constexpr (!DEEP) {
+            for (int t = 0; t < ktiles; ++t) {
+                const int cur = t & 1;
+                if (mma) mfma_steps(cur, 0, S / 2);
+                if (t + 1 < ktiles) {
+                    // registers hold stage t+1: decode into the free buffer,
+                    // then start stage t+2's loads
+                    la.store(As[cur ^ 1]);
+                    lb.store(Bs[cur ^ 1]);
+                    if (t + 2 < ktiles) {
+                        la.template load<FULL>((t + 2) * BK);
+                        lb.template load<FULL>((t + 2) * BK);
+                    }
                 }
+                if (mma) mfma_steps(cur, S / 2, S);
+                __syncthreads();
             }
-            if (mma) mfma_steps(cur, S / 2, S);
-            __syncthreads();
+        } else {
+            // set 0 holds the even stages, set 1 the odd ones: stage t
+            // decodes stage t+1's set into the free buffer, then loads stage
+            // t+3 into that set
+            auto stage = [&](int t, LA &xa, LB &xb) {
+                const int cur = t & 1;
+                if (mma) mfma_steps(cur, 0, S / 2);
+                if (t + 1 < ktiles) {
+                    xa.store(As[cur ^ 1]);
+                    xb.store(Bs[cur ^ 1]);
+                    if (t + 3 < ktiles) {
+                        xa.template load<FULL>((t + 3) * BK);
+                        xb.template load<FULL>((t + 3) * BK);
+                    }
+                }
+                if (mma) mfma_steps(cur, S / 2, S);
+                __syncthreads();
+            };
+            for (int t = 0; t < ktiles; t += 2) {
+                stage(t, la1, lb1);
+                if (t + 1 < ktiles) stage(t + 1, la, lb);
+            }
         }
     }
 
@@ -1011,7 +1045,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, i
     if (full)
         C::template run<true>(la, lb, K, As, Bs, acc);
     else
-        C::template run<false, true>(la, lb, K, As, Bs, acc, fn_act);
+        C::template run<false, true, true>(la, lb, K, As, Bs, acc, fn_act);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
