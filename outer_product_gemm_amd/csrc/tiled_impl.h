@@ -965,7 +965,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
             LB lb2[2] = {lb, lb};
             C::run_pipe(la2, lb2, K, As, Bs, acc);
         } else {
-            C::template run<true>(la, lb, K, As, Bs, acc);
+            C::template run<true, false, true>(la, lb, K, As, Bs, acc);
         }
     } else {
         C::template run<false>(la, lb, K, As, Bs, acc);
