@@ -965,7 +965,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
             LB lb2[2] = {lb, lb};
             C::run_pipe(la2, lb2, K, As, Bs, acc);
         } else {
-            C::template run<true, false, true>(la, lb, K, As, Bs, acc);
+            // loads two stages ahead (not q3_K with 32-row stages, whose
+            // decode registers leave no room for the second set)
+            constexpr bool kDeep = BK == 16 || AT != OUTPROD_TYPE_Q3_K;
+            C::template run<true, false, kDeep>(la, lb, K, As, Bs, acc);
         }
     } else {
         C::template run<false>(la, lb, K, As, Bs, acc);
