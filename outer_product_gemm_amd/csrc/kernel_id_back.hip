@@ -268,28 +268,28 @@ double expected_tiles_per_expert(const IdProblem &p, int bn) {
 }
 
 // Grouped-kernel configurations the automatic choice considers: 64 x 64,
-// 128 x 80 and 128 x 128 tiles of 4 waves and 128 x 128 tiles of 8 waves
-// whose waves each span the 128 slots (the others can be forced), with their
-// rates in the grouped kernel (TileCfg::eff's unit).  The rates come from
-// graph-timed launches of each configuration, forced, on 64 q4_K experts, 8
-// of 64 routed, 512 tokens (ne00 2560 x K 1024: 323 / 334 / 403 / 322 us;
-// ne00 1024 x K 2560: 357 / 407 / 439 / 322 us, routing included), divided
-// into the work the cost model below counts for each; partly filled tiles
-// and the gathered slot columns make the wider slot tiles relatively slower
-// here than in a dense OUT_PROD, except where every wave skips the same
-// empty blocks.
+// 128 x 80 and 128 x 128 tiles of 4 waves, and 128 x 128 and 128 x 96 tiles
+// of 8 waves that each span all the slot rows (the others can be forced),
+// with their rates in the grouped kernel (TileCfg::eff's unit).  The rates
+// come from graph-timed launches of each configuration, forced, on 64 q4_K
+// experts, 8 of 64 routed, 512 tokens (ne00 2560 x K 1024: 323 / 334 / 403 /
+// 322 / 270 us; ne00 1024 x K 2560: 357 / 407 / 439 / 322 / 303 us, routing
+// included), divided into the work the cost model below counts for each;
+// partly filled tiles and the gathered slot columns make the wider slot
+// tiles relatively slower here than in a dense OUT_PROD, except where every
+// wave skips the same empty blocks.
 struct IdAutoCfg {
     int cfg;
     double eff;
 };
-constexpr IdAutoCfg kIdAuto[] = {{4, 10.6}, {12, 8.35}, {0, 11.45}, {15, 14.5}};
+constexpr IdAutoCfg kIdAuto[] = {{4, 10.6}, {12, 8.35}, {0, 11.45}, {15, 14.5}, {17, 11.6}};
 
 // l->variant on entry: forced configuration + 1 (an index into kCfgs that is
 // built for the grouped kernel), or 0 for automatic.  The automatic choice
 // minimizes the estimated time: workgroups x tile area x K / eff, slowed in
 // proportion when there are fewer than 2560 waves (10 per CU: the CUs' MFMA
 // pipes are not kept busy), with the workgroup count from the expected tiles
-// per expert.  The shapes above run best with the 8-wave 128 x 128 tiles.
+// per expert.  The shapes above run best with the 8-wave 128 x 96 tiles.
 bool plan_id_back(IdProblem &p, Launch *l) {
     using namespace tiled;
     int best = -1;

@@ -1094,13 +1094,14 @@ struct TileCfg {
 // 14: 80 x 256, 8 waves of 80 x 32 (16x16x4) in one row, 32-row stages --
 //     m5120 x n1024 in 256 tiles with half the a decode per flop of 8 (the
 //     planner rates it per a type: cfg_eff)
-// Grouped MUL_MAT_ID_BACK only (past kNumCfgs): 128-slot tiles that every
-// wave spans whole, so in a tile holding an expert's few dozen slots every
-// wave skips the same MFMA blocks:
+// Grouped MUL_MAT_ID_BACK only (past kNumCfgs): slot tiles that every wave
+// spans whole, so in a tile holding an expert's few dozen slots every wave
+// skips the same MFMA blocks:
 // 15: 128 x 128, 8 waves of 16 x 128 (16x16x4)
 // 16: 128 x 128, 4 waves of 32 x 128 (16x16x4)
+// 17: 128 x 96,  8 waves of 16 x 96 (16x16x4)
 // (64 x 128 tiles of 4 waves and 32-row stages of 15 ran at half its rate
-// on the 64-expert shapes below.)
+// on the 64-expert shapes.)
 constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 16, 12.4f},
     {16, 5, 2, 2, 4, 16, 11.5f},
@@ -1119,6 +1120,7 @@ constexpr TileCfg kCfgs[] = {
     {16, 5, 2, 1, 8, 32, 12.5f},
     {16, 1, 8, 8, 1, 16, 10.0f},
     {16, 2, 8, 4, 1, 16, 10.0f},
+    {16, 1, 6, 8, 1, 16, 10.0f},
 };
 // The OUT_PROD menu: configurations 0 .. kNumCfgs-1.
 constexpr int kNumCfgs = 15;
@@ -1157,7 +1159,7 @@ const void *tiled_fn(int variant, bool bt) {
 
 // Tile configurations the grouped MUL_MAT_ID_BACK kernel is built for
 // (indices into kCfgs): 64-, 80- and 128-slot tiles, 16- and 32-row stages.
-constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13, 15, 16};
+constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13, 15, 16, 17};
 constexpr int kNumIdCfgs = sizeof(kIdCfgs) / sizeof(kIdCfgs[0]);
 
 template <int AT, int C>
@@ -1180,6 +1182,7 @@ const void *id_fn(int cfg) {
     case 13: return id_cfg_fn<AT, 13>();
     case 15: return id_cfg_fn<AT, 15>();
     case 16: return id_cfg_fn<AT, 16>();
+    case 17: return id_cfg_fn<AT, 17>();
     default: return nullptr;
     }
 }
