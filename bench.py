@@ -19,11 +19,9 @@ launch against the MI355X peak (fp32 MFMA 157.3 TFLOP/s, HBM 8 TB/s);
 workload on this host's cores.
 """
 import argparse
-import hashlib
 import json
 import os
 import platform
-import re
 import sys
 import time
 
@@ -105,14 +103,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _code_only(text: str) -> str:
-    """C/C++ source with comments removed and whitespace collapsed, so that
-    editing a comment does not count as a kernel change."""
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return " ".join(text.split())
-
-
 # The sources each kernel family's code and launch plan come from (the host
 # file api.cpp chooses the plan; the family files hold the kernels).
 FAMILY_SOURCES = {
@@ -128,13 +118,8 @@ FAMILY_SOURCES["tiled_id"] = FAMILY_SOURCES["tiled"] + ["kernel_id_back.hip"]
 def kernel_source_hash(files=None):
     """Hash of the code (not the comments) of the given csrc files (default:
     every kernel and host source)."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "outer_product_gemm_amd", "csrc")
-    names = sorted(files) if files else sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".cpp")))
-    for name in names:
-        with open(os.path.join(csrc, name), encoding="utf-8") as f:
-            h.update((name + "\n" + _code_only(f.read())).encode())
-    return h.hexdigest()[:16]
+    from outer_product_gemm_amd.build import source_hash
+    return source_hash(files)
 
 
 def is_moe(inst):
@@ -434,6 +419,7 @@ def main():
         "kernel_source_hash": src_hash,
         "kernel_family_hash": fam_hash,
         "git_rev": git_rev(),
+        "library_build": library_build(src_hash),
         "seeds": {i.name: int(i.seed) for i in insts},
         "nonfinite_outputs": nonfinite,
         "measured_peaks": measured,
@@ -445,19 +431,26 @@ def main():
 
 
 def git_rev():
-    """The checkout's commit (with "-dirty" for local changes), or None where
-    the tree carries no git metadata."""
-    import subprocess
-    try:
-        rev = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
-                             text=True, timeout=10)
-        if rev.returncode != 0:
-            return None
-        dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
-                               capture_output=True, text=True, timeout=10)
-        return rev.stdout.strip() + ("-dirty" if dirty.stdout.strip() else "")
-    except (OSError, subprocess.SubprocessError):
+    from outer_product_gemm_amd.build import git_rev as rev
+    return rev()
+
+
+def library_build(src_hash):
+    """What the loaded liboutprod.so was built from (its build stamp): the
+    sources' code hash then, whether it equals the sources' hash now, and the
+    commit checked out at build time (the only revision a tree copied without
+    git metadata carries)."""
+    from outer_product_gemm_amd.build import read_stamp
+    stamp = read_stamp()
+    if stamp is None:
+        log("warning: liboutprod.so has no build stamp")
         return None
+    ok = stamp.get("source_hash") == src_hash
+    if not ok:
+        log("warning: liboutprod.so was built from sources with hash %s, the sources now hash to %s"
+            % (stamp.get("source_hash"), src_hash))
+    return {"source_hash": stamp.get("source_hash"), "matches_sources": ok,
+            "git_rev_at_build": stamp.get("git_rev")}
 
 
 def load_calib():
