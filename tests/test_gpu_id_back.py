@@ -165,6 +165,16 @@ def test_id_back_routing_paths_agree():
     assert np.array_equal(small.view(np.uint32), gpu[:2000].view(np.uint32))
 
 
+@pytest.mark.parametrize("n_tok", [8192, 8193])
+def test_id_back_routing_limit(n_tok):
+    """2 slots per token: 16384 slots (the most the one-block routing takes)
+    and 16386 (the three routing kernels), against the oracle."""
+    inst = synth.make_moe_instance("lim", synth.Q4_0, 64, 16, 12, 2, n_tok, seed_of("lim", n_tok))
+    G.log("case id_back routing limit", n_tok * 2, "slots")
+    gpu, _ = run_id(inst)
+    check_id(inst, gpu)
+
+
 def test_id_back_invalid_ids_give_nan_rows():
     inst = synth.make_moe_instance("bad", synth.F32, 64, 40, 5, 2, 30, seed_of("bad"))
     ids = inst.ids.copy()
