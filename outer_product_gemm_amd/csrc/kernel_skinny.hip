@@ -623,9 +623,13 @@ bool plan_skinny(const Problem &p, Launch *l) {
         // segments (64-column strips) read fastest; wider b, and a with
         // several 32-column blocks (per-head products), run 32-column strips.
         // The 4x4x1 kernel is a few % faster for ranks <= 4 over 256-byte
-        // segments and slower everywhere else.
+        // segments and slower everywhere else.  K-contiguous b (one column
+        // per lane) runs 16 waves of 16x16x4 with 8-step batches: at the
+        // split counts the planner picks, 3-17% faster than 8 waves of
+        // 4x4x1 or 16x16x4 for ranks 4-24, K 4096-17408 (LoRA dh: 4B
+        // 13.7 -> 11.3 us, 27B 27.3 -> 23.7 us).
         if (p.b_kt)
-            cfg = p.M <= 8 ? 6 : 0;  // K-contiguous b: one column per lane
+            cfg = 5;
         else if (p.M > 32)
             cfg = 1;
         else if (p.N <= 4096)
