@@ -311,6 +311,15 @@ bool plan_id_back(IdProblem &p, Launch *l) {
             }
         }
     }
+    if (l->variant <= 0 && best == 17) {
+        // 96-slot tiles: three 8-wave workgroups share a CU with 16-row
+        // stages (78 VGPRs); with fewer than that per CU (about 16 waves)
+        // the 32-row stages hide more of a stage's latency (64 q4_K experts,
+        // 512 tokens: ne00 1024 x K 2560, 512 workgroups: 301 -> 286 us;
+        // ne00 2560 x K 1024, 1280 workgroups: 268 -> 283 us the other way)
+        const double wgs = (double)((p.M + 127) / 128) * (double)p.n_expert * expected_tiles_per_expert(p, 96);
+        if (wgs * 8 < 24.0 * 256) best = 18;
+    }
     const TileCfg &c = kCfgs[best];
     set_layout(p, c.bn());
     l->kernel = OUTPROD_KERNEL_TILED;

@@ -1100,6 +1100,7 @@ struct TileCfg {
 // 15: 128 x 128, 8 waves of 16 x 128 (16x16x4)
 // 16: 128 x 128, 4 waves of 32 x 128 (16x16x4)
 // 17: 128 x 96,  8 waves of 16 x 96 (16x16x4)
+// 18: as 17 with 32-row stages
 // (64 x 128 tiles of 4 waves and 32-row stages of 15 ran at half its rate
 // on the 64-expert shapes.)
 constexpr TileCfg kCfgs[] = {
@@ -1121,6 +1122,7 @@ constexpr TileCfg kCfgs[] = {
     {16, 1, 8, 8, 1, 16, 10.0f},
     {16, 2, 8, 4, 1, 16, 10.0f},
     {16, 1, 6, 8, 1, 16, 10.0f},
+    {16, 1, 6, 8, 1, 32, 10.0f},
 };
 // The OUT_PROD menu: configurations 0 .. kNumCfgs-1.
 constexpr int kNumCfgs = 15;
@@ -1159,7 +1161,7 @@ const void *tiled_fn(int variant, bool bt) {
 
 // Tile configurations the grouped MUL_MAT_ID_BACK kernel is built for
 // (indices into kCfgs): 64-, 80- and 128-slot tiles, 16- and 32-row stages.
-constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13, 15, 16, 17};
+constexpr int kIdCfgs[] = {2, 4, 1, 0, 8, 10, 11, 12, 13, 15, 16, 17, 18};
 constexpr int kNumIdCfgs = sizeof(kIdCfgs) / sizeof(kIdCfgs[0]);
 
 template <int AT, int C>
@@ -1183,6 +1185,7 @@ const void *id_fn(int cfg) {
     case 15: return id_cfg_fn<AT, 15>();
     case 16: return id_cfg_fn<AT, 16>();
     case 17: return id_cfg_fn<AT, 17>();
+    case 18: return id_cfg_fn<AT, 18>();
     default: return nullptr;
     }
 }

@@ -180,8 +180,8 @@ def test_forced_kernels():
     for cfg in range(15):
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg
-    # 15 to 17 are built for the grouped MUL_MAT_ID_BACK kernel only
-    for cfg in (15, 16, 17, 40):
+    # 15 to 18 are built for the grouped MUL_MAT_ID_BACK kernel only
+    for cfg in (15, 16, 17, 18, 40):
         assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, cfg))] == "E_KERNEL"
 
 
@@ -309,7 +309,7 @@ def test_id_back_plans_and_refusals():
     p = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb)
     assert p["kernel_name"] == "tiled" and p["slices"] == 80 and p["flops"] == 2 * 512 * 96 * 80
     assert p["workspace_bytes"] > 0 and p["grid"] >= 1
-    for cfg in (0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17):
+    for cfg in (0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17, 18):
         q = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb,
                                     B.kernel_code(B.KERNEL_TILED, cfg))
         assert q["variant"] == cfg
