@@ -304,6 +304,20 @@ def id_plan(inst, a=A, g=G_, ids=I_, d=D, ne=None, nb=None, kernel=0):
     return B.id_back_plan_status(a, inst.a_type, g, ids, d, ne or inst.ne, nb or inst.nb, kernel)
 
 
+def test_id_back_automatic_tiles():
+    """The grouped kernel's automatic tiles on the 64-expert shapes: 128 x 96
+    slot tiles, with 32-row stages where fewer than three 8-wave workgroups
+    per CU would be resident (the down-projection gradient's 512 tiles)."""
+    for name, cfg, bk in (("moe_up_back_q4_K", 17, 16), ("moe_down_back_q4_K", 18, 32)):
+        inst = synth.moe_workload(name)
+        p = B.out_prod_id_back_plan(A, inst.a_type, G_, I_, D, inst.ne, inst.nb)
+        assert (p["variant"], p["tile_m"], p["tile_n"], p["tile_k"], p["block"]) == (cfg, 128, 96, bk, 512), (name, p)
+    # few tokens: slot tiles stay small (64 x 64)
+    inst = synth.make_moe_instance("few", synth.Q4_K, 2560, 1024, 64, 8, 16, 1)
+    p = B.out_prod_id_back_plan(A, inst.a_type, G_, I_, D, inst.ne, inst.nb)
+    assert p["tile_n"] <= 80, p
+
+
 def test_id_back_plans_and_refusals():
     inst = synth.make_moe_instance("abi", synth.Q4_K, 512, 96, 8, 2, 40, 1)
     p = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb)
