@@ -237,22 +237,25 @@ int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
  * Alignment as for out_prod (a's rules for as; 4 bytes elsewhere).  At most
  * 512 experts.  All pointers are device pointers owned by the caller.
  *
- * The slots are grouped by expert on the device (three small routing kernels,
- * tables in the stream's workspace -- see "Split K and the workspace" above,
- * including OUTPROD_E_CAPTURE and OUTPROD_E_WORKSPACE), then one tiled launch
- * runs every expert's
- * slots; 4 launches on `stream`.  A slot whose id is outside [0, n_expert) gets
- * a row of NaN (ids are device data; there is no host-side check).  K == 0
- * writes zeros without reading ids; no slots or ne00 == 0: no work.
- * Deterministic: slots keep their order within an expert and each dst row has
- * one writer.  Returns OUTPROD_OK or a status (checks as for out_prod).
+ * The slots are grouped by expert on the device (one routing kernel up to
+ * 16384 slots, three beyond; tables in the stream's workspace -- see "Split K
+ * and the workspace" above, including OUTPROD_E_CAPTURE and
+ * OUTPROD_E_WORKSPACE), then one tiled launch runs every expert's slots: 2 or
+ * 4 launches on `stream`.  A slot whose id is outside [0, n_expert) gets a row
+ * of NaN (ids are device data; there is no host-side check).  K == 0 writes
+ * zeros without reading ids; no slots or ne00 == 0: no work.  Deterministic:
+ * each dst row has one writer and sums over K in a fixed order, whichever
+ * tile holds its slot (the one-kernel routing orders an expert's slots with
+ * atomics, the three-kernel routing keeps their order).  Returns OUTPROD_OK
+ * or a status (checks as for out_prod).
  */
 int out_prod_id_back(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
                      const int64_t ne[16], const int64_t nb[16], void *stream);
 
 /* out_prod_id_back with a forced tile configuration: kernel = OUTPROD_KERNEL_TILED
- * | (index + 1) << 8 with an index the grouped kernel is built for (0, 1, 2, 4),
- * or OUTPROD_KERNEL_AUTO. */
+ * | (index + 1) << 8 with an index the grouped kernel is built for (0, 1, 2, 4,
+ * 8, 10, 11, 12, 13, and 15-18: slot tiles of 128, 128, 96 and 96 rows built
+ * for the grouped kernel only), or OUTPROD_KERNEL_AUTO. */
 int out_prod_id_back_ex(const void *as, int as_type, const float *g, const int32_t *ids, float *dst,
                         const int64_t ne[16], const int64_t nb[16], void *stream, int kernel);
 
