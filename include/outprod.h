@@ -155,7 +155,9 @@ int out_prod(const void *a, int a_type, const float *b, float *dst,
                                    gradients), for a narrow f32 b (operand swap) and for f32
                                    problems with too few output tiles for the tiled kernel */
 #define OUTPROD_KERNEL_TILED 2  /* LDS-staged fp32 tiles, MFMA 32x32x2 or 16x16x4, any a
-                                   type and shape; a menu of tile configurations */
+                                   type and shape; a menu of tile configurations (0-14, and
+                                   19-20: 272 x 128 tiles whose loads and decode run on 8
+                                   waves of their own) */
 #define OUTPROD_KERNEL_ZERO 3   /* K == 0: writes zeros */
 #define OUTPROD_KERNEL_NONE 4   /* empty dst: nothing to do */
 
@@ -210,8 +212,9 @@ int out_prod_plan(const void *a, int a_type, const float *b, const float *dst,
  * tiles along i0 means i0 fastest), as reported in outprod_plan.group_m; 0
  * lets the library choose.  A family, configuration, split or order that
  * cannot run the problem returns OUTPROD_E_KERNEL (e.g. SKINNY for a
- * quantized a, an unknown configuration index, more ranges than K rows,
- * partials beyond the workspace, an order with another family).
+ * quantized a, an unknown configuration index -- the tiled family's are
+ * 0-14 and 19-20 --, more ranges than K rows, partials beyond the workspace,
+ * an order with another family).
  */
 int out_prod_ex(const void *a, int a_type, const float *b, float *dst,
                 const int64_t ne[12], const int64_t nb[12], void *stream, int kernel);

@@ -41,6 +41,10 @@ STATUS = {
 }
 KERNEL_AUTO, KERNEL_SKINNY, KERNEL_TILED, KERNEL_ZERO, KERNEL_NONE = 0, 1, 2, 3, 4
 KERNEL_NAMES = {1: "skinny", 2: "tiled", 3: "zero", 4: "none"}
+# Configuration indices each family accepts when forced (out_prod_ex bits
+# 8-15): the tiled OUT_PROD menu, the grouped MUL_MAT_ID_BACK kernel's tiles.
+TILED_CONFIGS = tuple(range(15)) + (19, 20)
+ID_CONFIGS = (0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17, 18)
 
 
 def kernel_code(family: int, config: int = None, splits: int = None, group_m: int = None) -> int:

@@ -25,10 +25,19 @@ constexpr double kSplitBytesPerUs = 4.0e6;
 // n1024: q3_K 1576 -> 1551 us, q4_K 1486 -> 1470, q5_K 1501 -> 1482, q6_K
 // 1529 -> 1501), slower where the decode is cheap (f32 1359 -> 1437, f16
 // 1384 -> 1429, bf16 1371 -> 1428) and about even for the other types.
+//
+// The 272 x 128 tile with loader waves (19: loads one stage ahead, 20: two)
+// is faster than configuration 9 for every type at m17408 k5120 n1024; 20
+// is the faster of the two for q4_0, q5_0, q6_K and q8_0 (1-2%, 10-11
+// 16-bit or byte loads per group), 19 for the others.
 double cfg_eff(int cfg, int a_type) {
     const bool sub_scaled_k = a_type == OUTPROD_TYPE_Q3_K || a_type == OUTPROD_TYPE_Q4_K ||
                               a_type == OUTPROD_TYPE_Q5_K || a_type == OUTPROD_TYPE_Q6_K;
+    const bool deep_loads = a_type == OUTPROD_TYPE_Q4_0 || a_type == OUTPROD_TYPE_Q5_0 ||
+                            a_type == OUTPROD_TYPE_Q6_K || a_type == OUTPROD_TYPE_Q8_0;
     if (cfg == 14 && !sub_scaled_k) return 11.9;
+    if (cfg == 19 && deep_loads) return 12.4;
+    if (cfg == 20 && !deep_loads) return 12.4;
     return kCfgs[cfg].eff;
 }
 
@@ -73,12 +82,13 @@ bool plan_tiled(const Problem &p, Launch *l) {
     // candidate split counts: forced, or 1 .. max_splits
     const int s_lo = forced_splits > 0 ? forced_splits : 1;
     const int s_hi = forced_splits > 0 ? forced_splits : max_splits(p);
-    const int c_lo = v > 0 ? v - 1 : 0, c_hi = v > 0 ? v - 1 : kNumCfgs - 1;
-    if (v > kNumCfgs) return false;
+    const int c_lo = v > 0 ? v - 1 : 0, c_hi = v > 0 ? v - 1 : kNumAllCfgs - 1;
+    if (v > 0 && !dense_cfg(v - 1)) return false;
     best = c_lo;
     double best_cost = 0;
     bool first = true;
     for (int i = c_lo; i <= c_hi; ++i) {
+        if (!dense_cfg(i)) continue;  // the grouped kernel's tiles
         for (int sp = s_lo; sp <= s_hi; ++sp) {
             const int64_t ks = forced_splits > 0 ? (p.K + sp - 1) / sp : split_rows(p.K, sp);
             const double c = cfg_cost(i, p, sp, ks);
@@ -105,7 +115,7 @@ bool plan_tiled(const Problem &p, Launch *l) {
     l->tile_n = c.bn();
     l->tile_k = c.bk;
     l->block = c.threads();
-    l->lds_bytes = 2 * c.bk * (lds_ld(c.bm(), c.mf) + lds_ld(c.bn(), c.mf)) * 4;
+    l->lds_bytes = c.stages() * c.bk * (lds_ld(c.bm(), c.mf) + lds_ld(c.bn(), c.mf)) * 4;
     l->splits = best_splits;
     l->ksplit = best_splits > 1 ? ksplit : p.K;
     l->grid = tm * tn * p.ne12 * p.ne13 * best_splits;

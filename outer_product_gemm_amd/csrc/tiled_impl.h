@@ -640,7 +640,6 @@ __host__ __device__ constexpr int lds_ld(int bw, int mf) {
 }
 
 // ---------------------------------------------------------------- kernel
-
 // One workgroup's BM x BN tile: the K loop shared by the OUT_PROD kernel and
 // the grouped MUL_MAT_ID_BACK kernel.  WGM x WGN waves, each with FM x FN
 // MFMA blocks of MF x MF; BK rows of K per pipeline stage.
@@ -897,6 +896,129 @@ struct TileCore {
         }
     }
 
+    // Wave-specialized K loop: the WGM x WGN multiplying waves only read
+    // operand fragments from LDS and issue MFMAs; P more waves (threads
+    // T .. T + 64P - 1, which own the loaders) load and decode.  Three LDS
+    // stages form a ring; the loaders keep D raw register sets.
+    // - Loader round r (r = -1, 0, ...) writes stage r + 2 into buffer
+    //   (r + 2) % 3, then issues the loads of stage r + 2 + D into the set it
+    //   freed, and ends with barrier X_r (the prologue writes stage 0 and
+    //   passes one barrier first).
+    // - A multiplying wave passes X_{t-1} after the MFMAs of stage t's first
+    //   step.  Between X_{t-1} and X_t it reads stages t and t + 1 (buffers
+    //   t % 3 and (t + 1) % 3) while the loaders fill (t + 2) % 3, whose
+    //   previous stage (t - 1) it finished before X_{t-1}; stage t + 1 was
+    //   written before X_{t-1}.
+    // - Its fragments are double-buffered across stage boundaries, so the
+    //   matrix core has the step's MFMAs queued while the wave waits at a
+    //   barrier.  Every wave passes 1 + ktiles barriers.
+    // The sum over k has the same order as in run (the MFMA steps in k
+    // order), so the result is the same bits.  For the column-of-waves tile
+    // this takes the decode off the multiplying waves, whose 68 accumulator
+    // registers leave no room for the pipelined loop.  What still costs:
+    // with the loaders' decode and LDS writes switched off (builds kept out
+    // of the library) the m17408 q4_K launch runs 1292 us instead of 1441
+    // us, with the loads alone kept 1287 us; the loader waves by themselves
+    // need 492 us -- their work competes with the MFMA waves on the same
+    // SIMDs rather than holding them up.  Per-buffer LDS counters polled in
+    // place of the barriers ran slower (1476 us).
+    template <bool FULL, int P, int D, class LA, class LB>
+    __device__ static void run_ws(LA &la, LB &lb, int K, float (&As)[3][BK][LDA],
+                                  float (&Bs)[3][BK][LDB], acc_t (&acc)[FM][FN]) {
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const int ktiles = (K + BK - 1) / BK;
+        if (wave >= WGM * WGN) {
+            // D register sets: set (s % D) holds stage s from its loads until
+            // its decode, D rounds later
+            LA la1 = la;
+            LB lb1 = lb;
+            la.template load<FULL>(0);
+            lb.template load<FULL>(0);
+            la.store(As[0]);
+            lb.store(Bs[0]);
+            if (ktiles > 1) {
+                (D == 2 ? la1 : la).template load<FULL>(BK);
+                (D == 2 ? lb1 : lb).template load<FULL>(BK);
+            }
+            if (D == 2 && ktiles > 2) {
+                la.template load<FULL>(2 * BK);
+                lb.template load<FULL>(2 * BK);
+            }
+            __syncthreads();
+            // round r: stage r + 2 into buffer (r + 2) % 3, then the loads
+            // of stage r + 2 + D into the set it freed
+            auto round = [&](int r, LA &xa, LB &xb) {
+                if (r + 2 < ktiles) {
+                    const int b = (r + 2) % 3;
+                    xa.store(As[b]);
+                    xb.store(Bs[b]);
+                    if (r + 2 + D < ktiles) {
+                        xa.template load<FULL>((r + 2 + D) * BK);
+                        xb.template load<FULL>((r + 2 + D) * BK);
+                    }
+                }
+                __syncthreads();
+            };
+            if constexpr (D == 2) {
+                for (int r = -1; r <= ktiles - 2; r += 2) {
+                    round(r, la1, lb1);
+                    if (r + 1 <= ktiles - 2) round(r + 1, la, lb);
+                }
+            } else {
+                for (int r = -1; r <= ktiles - 2; ++r) round(r, la, lb);
+            }
+            return;
+        }
+        const int lane = threadIdx.x & 63;
+        const int wm = wave % WGM, wn = wave / WGM;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < MM::NR; ++r) acc[i][j][r] = 0.f;
+        const int kq = lane / MF, col = lane % MF;
+        const int a_col = wm * WTM + col, b_col = wn * WTN + col;
+        float af[2][FM], bf[2][FN];
+        auto frag = [&](int buf, int st, float(&xa)[FM], float(&xb)[FN]) {
+            const int kr = MM::KS * st + kq;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) xa[i] = As[buf][kr][a_col + MF * i];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                xb[j] = Bs[buf][kr][(b_col + MF * j) ^ b_swizzle<BN>(MM::KS * st)];
+        };
+        __syncthreads();
+        frag(0, 0, af[0], bf[0]);
+        int cur = 0;
+        for (int t = 0; t < ktiles; ++t) {
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            static_for<S>([&](auto st_c) {
+                constexpr int st = decltype(st_c)::value, x = st & 1;
+                // the next step's fragments (after the last stage: a read of
+                // a buffer whose values are not used)
+                if constexpr (st + 1 < S)
+                    frag(cur, st + 1, af[x ^ 1], bf[x ^ 1]);
+                else
+                    frag(nxt, 0, af[x ^ 1], bf[x ^ 1]);
+                // keep those reads ahead of this step's MFMAs (the scheduler
+                // otherwise moves each read next to its use, one wait per
+                // MFMA pair)
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = MM::step(bf[x][j], af[x][i], acc[i][j]);
+                if constexpr (st == 0) {
+                    // the step's MFMAs go out before the barrier's wait
+                    __builtin_amdgcn_sched_barrier(0);
+                    __syncthreads();
+                }
+            });
+            cur = nxt;
+        }
+    }
+
     // Tile-relative dst position of accumulator (i, j, register r) of this
     // lane: column (along i0) and row (along i1).
     __device__ static int col_of(int i) {
@@ -909,13 +1031,15 @@ struct TileCore {
     }
 };
 
-template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT>
-__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int tiles_m,
-                                                               int tiles_n, int group_m) {
+// P > 0: P more waves that load and decode for the multiplying ones (run_ws).
+template <int AT, int MF, int FM, int FN, int WGM, int WGN, int BK, bool BT, int P = 0, int D = 1>
+__global__ __launch_bounds__(64 * (WGM * WGN + P)) void tiled_kernel(Problem p0, int tiles_m,
+                                                                     int tiles_n, int group_m) {
     typedef TileCore<MF, FM, FN, WGM, WGN, BK> C;
     constexpr int T = C::T, BM = C::BM, BN = C::BN;
-    __shared__ __attribute__((aligned(16))) float As[2][BK][C::LDA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK][C::LDB];
+    constexpr int NS = P > 0 ? 3 : 2;  // LDS stages
+    __shared__ __attribute__((aligned(16))) float As[NS][BK][C::LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[NS][BK][C::LDB];
 
     const int tid = threadIdx.x;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -942,13 +1066,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     // accumulators (not the column-of-waves tiles: with 68 accumulator
     // registers per wave they spill) and a step per a group plus two; q4_K
     // takes 16-value groups there when their last round fills whole waves
-    constexpr bool kPipeCfg = FM * FN * C::MM::NR <= 64;
+    constexpr bool kPipeCfg = P == 0 && FM * FN * C::MM::NR <= 64;
     constexpr int kG16 = BK * BM / 16;
     constexpr bool kWide = kPipeCfg && (kG16 % T == 0 || kG16 % T % 64 == 0);
-    typename ALoaderFor<AT, BM, BK, T, kWide>::type la;
-    typename std::conditional<BT, F32LoaderKT<BN, BK, T>, F32Loader<BN, BK, T, true>>::type lb;
-    la.init(s.a, p.nb01, M, K, m0, p.vec_a, tid);
-    lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tid);
+    // threads that run the loaders: all, or the P loader waves
+    constexpr int TL = P > 0 ? 64 * P : T;
+    const int tl = P > 0 ? tid - T : tid;
+    typename ALoaderFor<AT, BM, BK, TL, kWide>::type la;
+    typename std::conditional<BT, F32LoaderKT<BN, BK, TL>, F32Loader<BN, BK, TL, true>>::type lb;
+    la.init(s.a, p.nb01, M, K, m0, p.vec_a, tl);
+    lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tl);
 
     // whole tile in range, whole stages, 16-byte aligned operands: the loads
     // need no per-lane checks
@@ -959,7 +1086,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(Problem p0, int t
     typedef decltype(la) LA;
     typedef decltype(lb) LB;
     constexpr bool kPipe = kPipeCfg && LA::kPer + 2 <= C::S;
-    if (full) {
+    if constexpr (P > 0) {
+        if (full)
+            C::template run_ws<true, P, D>(la, lb, K, As, Bs, acc);
+        else
+            C::template run_ws<false, P, D>(la, lb, K, As, Bs, acc);
+        if (tid >= T) return;  // loader waves hold no accumulators
+    } else if (full) {
         if constexpr (kPipe) {
             LA la2[2] = {la, la};
             LB lb2[2] = {lb, lb};
@@ -1072,9 +1205,15 @@ struct TileCfg {
     // the busiest CU, from the q4_K/q8_0 27B-shape sweeps); the planner
     // compares (tiles per CU x tile area) / eff across configurations.
     float eff;
+    // Loader waves (0: every wave loads, decodes and multiplies; > 0: the
+    // wgm x wgn waves only multiply and ws more waves load and decode, with
+    // three LDS stages).
+    int ws = 0;
+    int wsd = 1;  // the loader waves' raw register sets (loads this many stages ahead)
     int bm() const { return mf * fm * wgm; }
     int bn() const { return mf * fn * wgn; }
-    int threads() const { return 64 * wgm * wgn; }
+    int threads() const { return 64 * (wgm * wgn + ws); }
+    int stages() const { return ws ? 3 : 2; }
 };
 
 // 0: 128 x 128, 4 waves of 64 x 64 (32x32x2) -- general purpose
@@ -1103,6 +1242,18 @@ struct TileCfg {
 // 18: as 17 with 32-row stages
 // (64 x 128 tiles of 4 waves and 32-row stages of 15 ran at half its rate
 // on the 64-expert shapes.)
+// OUT_PROD, with 8 more waves that only load and decode (run_ws; 1024
+// threads, three LDS stages: 156 KB, one workgroup per CU):
+// 19: as 9 (272 x 128, 8 multiplying waves of 272 x 16), loads one stage ahead
+// 20: as 19 with loads two stages ahead (two raw register sets)
+// -- m17408 x n1024.  Measured against 9 at m17408 k5120 n1024 (eager,
+// rotating inputs, best of two rounds, us): q4_K 1503 -> 1444, f32 1450 ->
+// 1384, f16 1451 -> 1378, bf16 1447 -> 1377, q4_1 1469 -> 1413, q5_1 1483
+// -> 1431, q2_K 1497 -> 1446, q3_K 1733 -> 1684, q5_K 1543 -> 1508, q8_0
+// 1581 -> 1526 (20), q4_0 1553 -> 1538 (20), q5_0 1608 -> 1601 (20), q6_K
+// 1661 -> 1647 (20).  The same split for the 160 x 128 and 80 x 256 tiles
+// of m5120 ran no faster than their pipelined loop (f32 1367 -> 1393 us,
+// q4_K 1469 -> 1467, q8_0 1469 -> 1684), so it is not in the menu.
 constexpr TileCfg kCfgs[] = {
     {32, 2, 2, 2, 2, 16, 12.4f},
     {16, 5, 2, 2, 4, 16, 11.5f},
@@ -1123,14 +1274,20 @@ constexpr TileCfg kCfgs[] = {
     {16, 2, 8, 4, 1, 16, 10.0f},
     {16, 1, 6, 8, 1, 16, 10.0f},
     {16, 1, 6, 8, 1, 32, 10.0f},
+    {16, 17, 1, 1, 8, 32, 12.6f, 8, 1},
+    {16, 17, 1, 1, 8, 32, 12.6f, 8, 2},
 };
-// The OUT_PROD menu: configurations 0 .. kNumCfgs-1.
+// The OUT_PROD menu: configurations 0 .. kNumCfgs-1 and the loader-wave ones.
 constexpr int kNumCfgs = 15;
+constexpr int kNumAllCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+__host__ __device__ constexpr bool dense_cfg(int c) {
+    return (c >= 0 && c < kNumCfgs) || (c >= 19 && c < kNumAllCfgs);
+}
 
 template <int AT, int C, bool BT>
 const void *cfg_fn() {
     constexpr TileCfg c = kCfgs[C];
-    return (const void *)&tiled_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk, BT>;
+    return (const void *)&tiled_kernel<AT, c.mf, c.fm, c.fn, c.wgm, c.wgn, c.bk, BT, c.ws, c.wsd>;
 }
 
 template <int AT, bool BT>
@@ -1150,6 +1307,8 @@ const void *tiled_fn(int variant) {
     case 12: return cfg_fn<AT, 12, BT>();
     case 13: return cfg_fn<AT, 13, BT>();
     case 14: return cfg_fn<AT, 14, BT>();
+    case 19: return cfg_fn<AT, 19, BT>();
+    case 20: return cfg_fn<AT, 20, BT>();
     default: return cfg_fn<AT, 0, BT>();
     }
 }

@@ -148,11 +148,13 @@ def test_tile_choice_at_the_27B_shapes():
     """The planner's measured tile choices at m5120 k17408 n1024 (one launch
     per CU round): the 80 x 256 tile (configuration 14, half the a decode per
     flop) for the K-quants with sub-block scales, 160 x 128 (configuration
-    8) for the types whose decode is cheap; 272 x 128 (configuration 9) for
-    m17408 k5120; the K-contiguous 27B input gradient like its type."""
+    8) for the types whose decode is cheap; 272 x 128 with loader waves for
+    m17408 k5120 (configuration 19, or 20 -- loads two stages ahead -- for
+    the types with many small loads per group); the K-contiguous 27B input
+    gradient like its type."""
     for name, cfg in (("q4_K_5120x17408", 14), ("q6_K_5120x17408", 14), ("q3_K_5120x17408", 14),
                       ("q5_K_5120x17408", 14), ("f32_5120x17408", 8), ("f16_5120x17408", 8),
-                      ("q8_0_5120x17408", 8), ("q4_0_5120x17408", 8), ("q4_K_17408x5120", 9),
+                      ("q8_0_5120x17408", 8), ("q4_0_5120x17408", 8), ("q4_K_17408x5120", 19),
                       ("q8_0_5120", 8), ("lora27B_dxW", 14)):
         inst_spec = synth.WORKLOADS[name]
         a_type, a_ne, b_ne = inst_spec[:3]
@@ -160,7 +162,13 @@ def test_tile_choice_at_the_27B_shapes():
         ne, nb = synth.make_ne_nb(a_type, a_ne, b_ne, kt)
         p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg and p["splits"] == 1, (name, p)
-        assert p["grid"] == (256 if cfg != 9 else 512), (name, p)
+        assert p["grid"] == (256 if cfg != 19 else 512), (name, p)
+    # m17408 k5120 n1024 for each type: 19, or 20 for q4_0, q5_0, q6_K, q8_0
+    for t in synth.TYPE_NAMES:
+        ne, nb = synth.make_ne_nb(t, (17408, 5120, 1, 1), (1024, 5120, 1, 1))
+        p = B.out_prod_plan(A, t, 0x40000000000, 0x80000000000, ne, nb)
+        want = 20 if t in (synth.Q4_0, synth.Q5_0, synth.Q6_K, synth.Q8_0) else 19
+        assert p["variant"] == want and p["block"] == 1024 and p["lds_bytes"] == 159744, (t, p)
 
 
 def test_forced_kernels():
@@ -177,11 +185,11 @@ def test_forced_kernels():
         assert p["kernel_name"] == "skinny" and p["variant"] == cfg
     assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_SKINNY, 13))] == "E_KERNEL"
     # every tiled configuration can be forced; an unknown one is refused
-    for cfg in range(15):
+    for cfg in B.TILED_CONFIGS:
         p = B.out_prod_plan(A, synth.F32, BB, D, ne, nb, B.kernel_code(B.KERNEL_TILED, cfg))
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg
     # 15 to 18 are built for the grouped MUL_MAT_ID_BACK kernel only
-    for cfg in (15, 16, 17, 18, 40):
+    for cfg in (15, 16, 17, 18, 21, 40):
         assert B.STATUS[plan(synth.F32, ne, nb, kernel=B.kernel_code(B.KERNEL_TILED, cfg))] == "E_KERNEL"
 
 
@@ -327,7 +335,8 @@ def test_id_back_plans_and_refusals():
         q = B.out_prod_id_back_plan(A, synth.Q4_K, G_, I_, D, inst.ne, inst.nb,
                                     B.kernel_code(B.KERNEL_TILED, cfg))
         assert q["variant"] == cfg
-    assert B.STATUS[id_plan(inst, kernel=B.kernel_code(B.KERNEL_TILED, 3))] == "E_KERNEL"
+    for cfg in (3, 19, 20):  # OUT_PROD-only configurations
+        assert B.STATUS[id_plan(inst, kernel=B.kernel_code(B.KERNEL_TILED, cfg))] == "E_KERNEL"
     assert B.STATUS[id_plan(inst, kernel=B.KERNEL_SKINNY)] == "E_KERNEL"
     assert B.STATUS[id_plan(inst, kernel=B.kernel_code(B.KERNEL_TILED, None, 2))] == "E_KERNEL"
     ne = list(inst.ne)

@@ -23,8 +23,10 @@ TYPES = [synth.F32, synth.F16, synth.BF16, synth.Q4_0, synth.Q4_1, synth.Q5_0, s
 # tiled configuration -> (tile height along i0, tile width along i1, stage rows)
 TILED = {0: (128, 128, 16), 1: (160, 128, 16), 2: (160, 64, 16), 3: (272, 128, 16), 4: (64, 64, 16),
          5: (272, 64, 16), 6: (256, 128, 16), 7: (128, 128, 32), 8: (160, 128, 32), 9: (272, 128, 32),
-         10: (160, 64, 32), 11: (64, 64, 32), 12: (128, 80, 16), 13: (64, 80, 16), 14: (80, 256, 32)}
-ID_CFGS = [0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17, 18]
+         10: (160, 64, 32), 11: (64, 64, 32), 12: (128, 80, 16), 13: (64, 80, 16), 14: (80, 256, 32),
+         19: (272, 128, 32), 20: (272, 128, 32)}
+ID_CFGS = list(B.ID_CONFIGS)
+assert sorted(TILED) == sorted(B.TILED_CONFIGS)
 COLUMN_CFGS = 13
 
 

@@ -97,7 +97,7 @@ def test_id_back_every_type(a_type):
     check_id(inst, gpu)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17, 18])
+@pytest.mark.parametrize("cfg", B.ID_CONFIGS)
 def test_id_back_every_configuration(cfg):
     inst = synth.make_moe_instance("c", synth.Q4_K, 768, 130, 9, 4, 150, seed_of("idc", cfg))
     gpu, _ = run_id(inst, kernel=B.kernel_code(B.KERNEL_TILED, cfg))
@@ -114,7 +114,7 @@ def test_id_back_whole_stages_every_type(a_type):
     check_id(inst, gpu)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4, 8, 10, 11, 12, 13, 15, 16, 17, 18])
+@pytest.mark.parametrize("cfg", B.ID_CONFIGS)
 @pytest.mark.parametrize("shape", [(768, 160, 9, 4, 150), (1024, 256, 5, 4, 150)])
 def test_id_back_whole_stages_every_configuration(cfg, shape):
     """Whole stages and aligned columns (and, where 768 is not a multiple of

@@ -82,7 +82,7 @@ def test_small_ragged(a_type, a_ne, b_ne, kernel):
     check_case(inst, kernel)
 
 
-@pytest.mark.parametrize("cfg", range(15))
+@pytest.mark.parametrize("cfg", B.TILED_CONFIGS)
 def test_every_tiled_configuration(cfg):
     """Each tiled configuration, forced, on ragged shapes of every a type
     (partial tiles in i0, i1 and K, broadcast slices)."""
@@ -369,7 +369,7 @@ def test_k_contiguous_b(a_type, a_ne, b_ne):
     check_case(inst)
 
 
-@pytest.mark.parametrize("cfg", range(15))
+@pytest.mark.parametrize("cfg", B.TILED_CONFIGS)
 def test_k_contiguous_b_every_tiled_configuration(cfg):
     code = B.kernel_code(B.KERNEL_TILED, cfg)
     for a_type, a_ne, b_ne in KT_CASES[3:]:

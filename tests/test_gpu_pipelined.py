@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 # stage rows (BK) of each tiled configuration, as out_prod_plan reports them
 STAGE_ROWS = {0: 16, 1: 16, 2: 16, 3: 16, 4: 16, 5: 16, 6: 16,
-              7: 32, 8: 32, 9: 32, 10: 32, 11: 32, 12: 16, 13: 16, 14: 32}
+              7: 32, 8: 32, 9: 32, 10: 32, 11: 32, 12: 16, 13: 16, 14: 32, 19: 32, 20: 32}
 # i0 = 512 (a multiple of every block size): full 64/80/128/160/256-wide
 # tiles and a ragged last one for 80, 160 and 272; i1 = 300: full
 # 64/80/128/256-row tiles and a ragged last one
@@ -65,7 +65,7 @@ def _stage_rows(inst, code):
                            inst.nb, code)["tile_k"]
 
 
-@pytest.mark.parametrize("cfg", range(15))
+@pytest.mark.parametrize("cfg", B.TILED_CONFIGS)
 def test_full_tiles_every_stage_count(cfg):
     code = B.kernel_code(B.KERNEL_TILED, cfg)
     bk = STAGE_ROWS[cfg]
@@ -84,7 +84,7 @@ def test_full_tiles_every_stage_count(cfg):
         assert res["ok"], (cfg, synth.TYPE_NAMES[a_type], K, kt, res)
 
 
-@pytest.mark.parametrize("cfg", [8, 9, 14, 0, 4])
+@pytest.mark.parametrize("cfg", [8, 9, 14, 0, 4, 19])
 def test_tile_order_every_way(cfg):
     """Tile orders forced through out_prod_ex and confirmed by the plan --
     i1 fastest (groups of 1), groups of 3 (a narrower last group when the
