@@ -54,6 +54,19 @@ def _cases():
             splits = int(rng.choice([0, 2, 4])) if K >= 256 else 0
             out.append(("column", synth.F32, m, n, K, int(rng.integers(1, 3)), bool(rng.integers(0, 2)), cfg,
                         splits, int(rng.integers(0, 2 ** 31 - 1))))
+    # the loader-wave tiles (19, 20): every a type, K from one row to a few
+    # stages (and its ring of three LDS stages wrapping several times),
+    # ragged tiles in both directions, broadcast slices, splits
+    for cfg in (19, 20):
+        for a_type in TYPES:
+            qk = synth.BLOCK_VALUES[a_type]
+            m = int(rng.integers(1, 600))
+            m = max(qk, (m + qk - 1) // qk * qk) if qk > 1 else m
+            n = int(rng.integers(1, 300))
+            K = int(rng.choice([1, 31, 32, 64, 96, 100, 224, int(rng.integers(1, 700))]))
+            splits = int(rng.choice([0, 2, 3])) if K >= 64 else 0
+            out.append(("tiled", a_type, m, n, K, int(rng.integers(1, 3)), bool(rng.integers(0, 2)), cfg,
+                        splits, int(rng.integers(0, 2 ** 31 - 1))))
     for cfg in ID_CFGS:
         a_type = int(rng.choice(TYPES))
         qk = synth.BLOCK_VALUES[a_type]
