@@ -88,7 +88,7 @@ __device__ __forceinline__ constexpr int b_swizzle(int k) {
 }
 
 // f32 rows.  SWZ: the tile is b's, stored with b_swizzle.
-template <int BW, int BK, int T, bool SWZ = false>
+template <int BW, int BK, int T, bool SWZ = false, bool PRE = false>
 struct F32Loader {
     static constexpr int kGroups = BK * BW / 4;
     static constexpr int kPer = (kGroups + T - 1) / T;
@@ -98,6 +98,9 @@ struct F32Loader {
     int w0, W, K, tid;
     bool vec;
     floatx4 r[kPer];
+    // PRE: each group's byte offset from the slice at k = 0, computed once
+    // per tile
+    int64_t off[PRE ? kPer : 1];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool vec_ok, int t) {
@@ -109,10 +112,30 @@ struct F32Loader {
         vec = vec_ok;
         tid = t;
     }
+    // PRE: the per-group offsets (called by the threads that run the loads,
+    // once per tile, before the first)
+    __device__ void pre() {
+        if constexpr (PRE) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int g = tid + T * j;
+                off[j] = (int64_t)(g / (BW / 4)) * ld + (int64_t)(w0 + 4 * (g % (BW / 4))) * 4;
+            }
+        }
+    }
     // FULL: the whole tile is in range and 16-byte aligned (uniform,
     // checked by the caller): unconditional vector loads.
     template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
+        if constexpr (PRE && FULL && !REDO) {
+            const uint8_t *bk = base + (int64_t)k0 * ld;
+            static_for<kPer>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr bool always = kGroups % T == 0 || T * (j + 1) <= kGroups;
+                if (always || tid + T * j < kGroups) r[j] = *(const floatx4 *)(bk + off[j]);
+            });
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
@@ -350,7 +373,7 @@ struct Q8Loader {
 
 // q4_K a: groups of GV (8 or 16) consecutive values of one 32-value
 // sub-block; a group's scale and min are decoded once for its GV values.
-template <int BM, int BK, int T, int GV>
+template <int BM, int BK, int T, int GV, bool PRE = false>
 struct Q4KLoader {
     static constexpr int kGroups = BK * BM / GV;
     static constexpr int kPer = (kGroups + T - 1) / T;
@@ -360,6 +383,11 @@ struct Q4KLoader {
     int64_t ld;
     int m0, M, K, tid;
     uint32_t dd[kPer], s0[kPer], s1[kPer], s2[kPer], q[kPer][NQ];
+    // PRE: each group's byte offset from the slice at k = 0 (its block
+    // header) and its codes' offset within the block, computed once per
+    // tile, so a stage's loads cost one 64-bit add per group
+    int64_t off[PRE ? kPer : 1];
+    int qo[PRE ? kPer : 1];
 
     __device__ void init(const uint8_t *slice, int64_t row_stride, int width, int k_len,
                          int col0, bool, int t) {
@@ -370,8 +398,42 @@ struct Q4KLoader {
         m0 = col0;
         tid = t;
     }
+    // PRE: the per-group offsets (called by the threads that run the loads,
+    // once per tile, before the first)
+    __device__ void pre() {
+        if constexpr (PRE) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int g = tid + T * j;
+                const int row = g / (BM / GV), m = m0 + GV * (g % (BM / GV));
+                const int w = m & 255;
+                off[j] = (int64_t)row * ld + (int64_t)(m >> 8) * 144;
+                qo[j] = 16 + 32 * ((w >> 5) >> 1) + (w & 31);
+            }
+        }
+    }
     template <bool FULL, bool REDO = false>
     __device__ void load(int k0) {
+        if constexpr (PRE && FULL && !REDO) {
+            // every group of the full rounds is in range: unconditional loads;
+            // only the last round's groups past kGroups are skipped
+            const uint8_t *bk = base + (int64_t)k0 * ld;
+            static_for<kPer>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr bool always = kGroups % T == 0 || T * (j + 1) <= kGroups;
+                if (always || tid + T * j < kGroups) {
+                    const uint32_t *hdr = (const uint32_t *)(bk + off[j]);
+                    const uint32_t *qs = (const uint32_t *)(bk + off[j] + qo[j]);
+                    dd[j] = hdr[0];
+                    s0[j] = hdr[1];
+                    s1[j] = hdr[2];
+                    s2[j] = hdr[3];
+#pragma unroll
+                    for (int e = 0; e < NQ; ++e) q[j][e] = qs[e];
+                }
+            });
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int g = group_index<kGroups, T, REDO>(tid + T * j);
@@ -568,32 +630,35 @@ struct early_chunks<BlockLoader<FmtQ6_K, BM, BK, T>> : std::true_type {};
 // where q4_K decodes groups of 16 values (one scale/min decode per 16); the
 // checked loop keeps groups of 8, whose tail round is spread more evenly
 // over the waves.
-template <int AT, int BM, int BK, int T, bool WIDE = false>
+// PRE: the loader keeps each group's offsets from one tile's setup (for the
+// loader waves, whose stage loop is short of VALU issue; the q4_K and f32
+// loaders implement it, the others ignore it).
+template <int AT, int BM, int BK, int T, bool WIDE = false, bool PRE = false>
 struct ALoaderFor;
-template <int BM, int BK, int T, bool WIDE>
-struct ALoaderFor<OUTPROD_TYPE_F32, BM, BK, T, WIDE> {
-    typedef F32Loader<BM, BK, T> type;
+template <int BM, int BK, int T, bool WIDE, bool PRE>
+struct ALoaderFor<OUTPROD_TYPE_F32, BM, BK, T, WIDE, PRE> {
+    typedef F32Loader<BM, BK, T, false, PRE> type;
 };
-template <int BM, int BK, int T, bool WIDE>
-struct ALoaderFor<OUTPROD_TYPE_Q8_0, BM, BK, T, WIDE> {
+template <int BM, int BK, int T, bool WIDE, bool PRE>
+struct ALoaderFor<OUTPROD_TYPE_Q8_0, BM, BK, T, WIDE, PRE> {
     typedef Q8Loader<BM, BK, T> type;
 };
-template <int BM, int BK, int T, bool WIDE>
-struct ALoaderFor<OUTPROD_TYPE_Q4_K, BM, BK, T, WIDE> {
-    typedef Q4KLoader<BM, BK, T, WIDE ? 16 : 8> type;
+template <int BM, int BK, int T, bool WIDE, bool PRE>
+struct ALoaderFor<OUTPROD_TYPE_Q4_K, BM, BK, T, WIDE, PRE> {
+    typedef Q4KLoader<BM, BK, T, WIDE ? 16 : 8, PRE> type;
 };
 
-template <int BM, int BK, int T, bool WIDE>
-struct ALoaderFor<OUTPROD_TYPE_F16, BM, BK, T, WIDE> {
+template <int BM, int BK, int T, bool WIDE, bool PRE>
+struct ALoaderFor<OUTPROD_TYPE_F16, BM, BK, T, WIDE, PRE> {
     typedef HalfLoader<false, BM, BK, T> type;
 };
-template <int BM, int BK, int T, bool WIDE>
-struct ALoaderFor<OUTPROD_TYPE_BF16, BM, BK, T, WIDE> {
+template <int BM, int BK, int T, bool WIDE, bool PRE>
+struct ALoaderFor<OUTPROD_TYPE_BF16, BM, BK, T, WIDE, PRE> {
     typedef HalfLoader<true, BM, BK, T> type;
 };
 #define OUTPROD_BLOCK_LOADER(TYPE, FMT)                  \
-    template <int BM, int BK, int T, bool WIDE>          \
-    struct ALoaderFor<TYPE, BM, BK, T, WIDE> {           \
+    template <int BM, int BK, int T, bool WIDE, bool PRE> \
+    struct ALoaderFor<TYPE, BM, BK, T, WIDE, PRE> {      \
         typedef BlockLoader<FMT, BM, BK, T> type;        \
     };
 OUTPROD_BLOCK_LOADER(OUTPROD_TYPE_Q4_0, FmtQ4_0)
@@ -640,6 +705,15 @@ __host__ __device__ constexpr int lds_ld(int bw, int mf) {
 }
 
 // ---------------------------------------------------------------- kernel
+
+// l.pre() where the loader has it (the loaders that keep per-group offsets).
+template <class L>
+__device__ __forceinline__ auto loader_pre(L &l, int) -> decltype(l.pre(), void()) {
+    l.pre();
+}
+template <class L>
+__device__ __forceinline__ void loader_pre(L &, long) {}
+
 // One workgroup's BM x BN tile: the K loop shared by the OUT_PROD kernel and
 // the grouped MUL_MAT_ID_BACK kernel.  WGM x WGN waves, each with FM x FN
 // MFMA blocks of MF x MF; BK rows of K per pipeline stage.
@@ -928,6 +1002,8 @@ struct TileCore {
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         const int ktiles = (K + BK - 1) / BK;
         if (wave >= WGM * WGN) {
+            loader_pre(la, 0);
+            loader_pre(lb, 0);
             // D register sets: set (s % D) holds stage s from its loads until
             // its decode, D rounds later
             LA la1 = la;
@@ -1072,8 +1148,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + P)) void tiled_kernel(Problem p0,
     // threads that run the loaders: all, or the P loader waves
     constexpr int TL = P > 0 ? 64 * P : T;
     const int tl = P > 0 ? tid - T : tid;
-    typename ALoaderFor<AT, BM, BK, TL, kWide>::type la;
-    typename std::conditional<BT, F32LoaderKT<BN, BK, TL>, F32Loader<BN, BK, TL, true>>::type lb;
+    typename ALoaderFor<AT, BM, BK, TL, kWide, (P > 0)>::type la;
+    typename std::conditional<BT, F32LoaderKT<BN, BK, TL>, F32Loader<BN, BK, TL, true, (P > 0)>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tl);
     lb.init(s.b, BT ? p.nb10 : p.nb11, N, K, n0, p.vec_b, tl);
 
