@@ -28,13 +28,13 @@ constexpr double kSplitBytesPerUs = 4.0e6;
 //
 // The 272 x 128 tile with loader waves (19: loads one stage ahead, 20: two)
 // is faster than configuration 9 for every type at m17408 k5120 n1024; 20
-// is the faster of the two for q4_0, q5_0, q6_K and q8_0 (1-2%, 10-11
-// 16-bit or byte loads per group), 19 for the others.
+// is the faster of the two for q4_0, q5_0 and q8_0 (1-2%), 19 for the
+// others (20 runs one set for q3_K, q5_K and q6_K, whose second set spilled).
 double cfg_eff(int cfg, int a_type) {
     const bool sub_scaled_k = a_type == OUTPROD_TYPE_Q3_K || a_type == OUTPROD_TYPE_Q4_K ||
                               a_type == OUTPROD_TYPE_Q5_K || a_type == OUTPROD_TYPE_Q6_K;
     const bool deep_loads = a_type == OUTPROD_TYPE_Q4_0 || a_type == OUTPROD_TYPE_Q5_0 ||
-                            a_type == OUTPROD_TYPE_Q6_K || a_type == OUTPROD_TYPE_Q8_0;
+                            a_type == OUTPROD_TYPE_Q8_0;
     if (cfg == 14 && !sub_scaled_k) return 11.9;
     if (cfg == 19 && deep_loads) return 12.4;
     if (cfg == 20 && !deep_loads) return 12.4;

@@ -1148,6 +1148,9 @@ __global__ __launch_bounds__(64 * (WGM * WGN + P)) void tiled_kernel(Problem p0,
     // threads that run the loaders: all, or the P loader waves
     constexpr int TL = P > 0 ? 64 * P : T;
     const int tl = P > 0 ? tid - T : tid;
+    // loader waves: the loaders keep each group's offsets from the tile's
+    // setup (PRE; for the other kernels it measured no faster, and slower on
+    // the split 64 x 64 tiles of m1536: 59.9 -> 67.3 us)
     typename ALoaderFor<AT, BM, BK, TL, kWide, (P > 0)>::type la;
     typename std::conditional<BT, F32LoaderKT<BN, BK, TL>, F32Loader<BN, BK, TL, true, (P > 0)>>::type lb;
     la.init(s.a, p.nb01, M, K, m0, p.vec_a, tl);
@@ -1163,10 +1166,13 @@ __global__ __launch_bounds__(64 * (WGM * WGN + P)) void tiled_kernel(Problem p0,
     typedef decltype(lb) LB;
     constexpr bool kPipe = kPipeCfg && LA::kPer + 2 <= C::S;
     if constexpr (P > 0) {
+        // two raw register sets do not fit beside q3_K, q5_K and q6_K's
+        // groups (they spilled 8-25 registers): one set for those
+        constexpr int kD = AT == OUTPROD_TYPE_Q3_K || AT == OUTPROD_TYPE_Q5_K || AT == OUTPROD_TYPE_Q6_K ? 1 : D;
         if (full)
-            C::template run_ws<true, P, D>(la, lb, K, As, Bs, acc);
+            C::template run_ws<true, P, kD>(la, lb, K, As, Bs, acc);
         else
-            C::template run_ws<false, P, D>(la, lb, K, As, Bs, acc);
+            C::template run_ws<false, P, kD>(la, lb, K, As, Bs, acc);
         if (tid >= T) return;  // loader waves hold no accumulators
     } else if (full) {
         if constexpr (kPipe) {

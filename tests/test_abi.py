@@ -150,7 +150,7 @@ def test_tile_choice_at_the_27B_shapes():
     flop) for the K-quants with sub-block scales, 160 x 128 (configuration
     8) for the types whose decode is cheap; 272 x 128 with loader waves for
     m17408 k5120 (configuration 19, or 20 -- loads two stages ahead -- for
-    the types with many small loads per group); the K-contiguous 27B input
+    q4_0, q5_0 and q8_0); the K-contiguous 27B input
     gradient like its type."""
     for name, cfg in (("q4_K_5120x17408", 14), ("q6_K_5120x17408", 14), ("q3_K_5120x17408", 14),
                       ("q5_K_5120x17408", 14), ("f32_5120x17408", 8), ("f16_5120x17408", 8),
@@ -163,11 +163,11 @@ def test_tile_choice_at_the_27B_shapes():
         p = B.out_prod_plan(A, a_type, 0x40000000000, 0x80000000000, ne, nb)
         assert p["kernel_name"] == "tiled" and p["variant"] == cfg and p["splits"] == 1, (name, p)
         assert p["grid"] == (256 if cfg != 19 else 512), (name, p)
-    # m17408 k5120 n1024 for each type: 19, or 20 for q4_0, q5_0, q6_K, q8_0
+    # m17408 k5120 n1024 for each type: 19, or 20 for q4_0, q5_0, q8_0
     for t in synth.TYPE_NAMES:
         ne, nb = synth.make_ne_nb(t, (17408, 5120, 1, 1), (1024, 5120, 1, 1))
         p = B.out_prod_plan(A, t, 0x40000000000, 0x80000000000, ne, nb)
-        want = 20 if t in (synth.Q4_0, synth.Q5_0, synth.Q6_K, synth.Q8_0) else 19
+        want = 20 if t in (synth.Q4_0, synth.Q5_0, synth.Q8_0) else 19
         assert p["variant"] == want and p["block"] == 1024 and p["lds_bytes"] == 159744, (t, p)
 
 
