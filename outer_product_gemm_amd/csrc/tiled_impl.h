@@ -991,11 +991,12 @@ struct TileCore {
     // this takes the decode off the multiplying waves, whose 68 accumulator
     // registers leave no room for the pipelined loop.  What still costs:
     // with the loaders' decode and LDS writes switched off (builds kept out
-    // of the library) the m17408 q4_K launch runs 1292 us instead of 1441
-    // us, with the loads alone kept 1287 us; the loader waves by themselves
-    // need 492 us -- their work competes with the MFMA waves on the same
-    // SIMDs rather than holding them up.  Per-buffer LDS counters polled in
-    // place of the barriers ran slower (1476 us).
+    // of the library) the m17408 q4_K launch ran 1292 us instead of 1441
+    // us, with the loads alone kept 1287 us.  The loader waves by themselves
+    // need 492 us, yet beside the MFMA waves their round is the stage's
+    // critical path: sleeps added to it lengthened the launch nearly one for
+    // one.  Per-buffer LDS counters polled in place of the barriers ran
+    // slower (1476 us).
     template <bool FULL, int P, int D, class LA, class LB>
     __device__ static void run_ws(LA &la, LB &lb, int K, float (&As)[3][BK][LDA],
                                   float (&Bs)[3][BK][LDB], acc_t (&acc)[FM][FN]) {
