@@ -143,12 +143,14 @@ __global__ __launch_bounds__(256) void id_place_kernel(IdProblem p) {
 // sorted list that holds each expert's slots in an order set by LDS atomics
 // (which tile a slot lands in changes no value: a dst row's sum depends
 // only on its own gradient column and the expert).  Thread t holds slots
-// t, t + 1024, ... in registers, their ids loaded at once.
+// t, t + 1024, ..., t + 1024 (R - 1) in registers, their ids loaded at once
+// (R: the launch's slot count over 1024, rounded up to a power of two).
+// One wave scans the per-expert counts 64 experts at a time with lane
+// shuffles (no block barriers inside the scan).
+template <int R>
 __global__ __launch_bounds__(1024) void id_route_kernel(IdProblem p) {
-    constexpr int R = kIdRouteFused / 1024;
     __shared__ int cnt[kIdMaxExperts];  // slots per expert, then the expert's offset
-    __shared__ int sc[1024], st[1024];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int E = (int)p.n_expert, nu = (int)p.n_used;
     const int total = (int)(p.n_used * p.n_tokens);
     int *ws = (int *)p.ws;
@@ -168,32 +170,39 @@ __global__ __launch_bounds__(1024) void id_route_kernel(IdProblem p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) rk[r] = ev[r] >= 0 ? atomicAdd(&cnt[ev[r]], 1) : -1;
     __syncthreads();
-    // per-expert offsets and the tile table (as id_scan_kernel)
-    const int c = tid < E ? cnt[tid] : 0;
-    const int nt = (c + p.bn - 1) / p.bn;
-    sc[tid] = c;
-    st[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < E; off <<= 1) {
-        const int a = tid >= off ? sc[tid - off] : 0;
-        const int b = tid >= off ? st[tid - off] : 0;
-        __syncthreads();
-        sc[tid] += a;
-        st[tid] += b;
-        __syncthreads();
-    }
-    if (tid < E) {
-        cnt[tid] = sc[tid] - c;
-        ws[p.off_offsets + tid] = sc[tid] - c;
-        const int t0 = st[tid] - nt;
-        for (int j = 0; j < nt; ++j) {
-            ws[p.off_tile_e + t0 + j] = tid;
-            ws[p.off_tile_r0 + t0 + j] = j * p.bn;
+    // per-expert offsets and the tile table (as id_scan_kernel), by wave 0:
+    // an inclusive scan over each run of 64 experts, plus the runs before
+    if (tid < 64) {
+        int carry_c = 0, carry_t = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int x = base + lane;
+            const int c = x < E ? cnt[x] : 0;
+            const int nt = (c + p.bn - 1) / p.bn;
+            int ic = c, it = nt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int a = __shfl_up(ic, off), b = __shfl_up(it, off);
+                if (lane >= off) {
+                    ic += a;
+                    it += b;
+                }
+            }
+            if (x < E) {
+                const int o = carry_c + ic - c, t0 = carry_t + it - nt;
+                cnt[x] = o;
+                ws[p.off_offsets + x] = o;
+                for (int j = 0; j < nt; ++j) {
+                    ws[p.off_tile_e + t0 + j] = x;
+                    ws[p.off_tile_r0 + t0 + j] = j * p.bn;
+                }
+            }
+            carry_c += __shfl(ic, 63);
+            carry_t += __shfl(it, 63);
         }
-    }
-    if (tid == E - 1) {
-        ws[p.off_offsets + E] = sc[tid];
-        ws[p.off_ntiles] = st[tid];
+        if (lane == 0) {
+            ws[p.off_offsets + E] = carry_c;
+            ws[p.off_ntiles] = carry_t;
+        }
     }
     __syncthreads();
     // the sorted list (as id_place_kernel)
@@ -209,6 +218,16 @@ __global__ __launch_bounds__(1024) void id_route_kernel(IdProblem p) {
             for (int m = 0; m < (int)p.M; ++m) d[m] = __builtin_nanf("");
         }
     }
+}
+
+// The routing kernel for a slot count (at most kIdRouteFused).
+const void *id_route_for(int64_t slots) {
+    static_assert(kIdRouteFused == 16 * 1024, "instantiations cover 1 to 16 rounds");
+    if (slots <= 1024) return (const void *)&id_route_kernel<1>;
+    if (slots <= 2048) return (const void *)&id_route_kernel<2>;
+    if (slots <= 4096) return (const void *)&id_route_kernel<4>;
+    if (slots <= 8192) return (const void *)&id_route_kernel<8>;
+    return (const void *)&id_route_kernel<16>;
 }
 
 const void *id_kernel_for(int a_type, int cfg) {
@@ -343,7 +362,7 @@ hipError_t launch_id_back(const IdProblem &p, const Launch &l, hipStream_t s) {
     void *args1[] = {&pp};
     hipError_t e;
     if (slots <= kIdRouteFused) {
-        e = hipLaunchKernel((const void *)&id_route_kernel, dim3(1), dim3(1024), args1, 0, s);
+        e = hipLaunchKernel(id_route_for(slots), dim3(1), dim3(1024), args1, 0, s);
     } else {
         e = hipLaunchKernel((const void *)&id_rank_kernel, dim3((unsigned)p.rank_blocks), dim3(kIdRankBlock),
                             args1, 0, s);
