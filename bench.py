@@ -49,6 +49,8 @@ COMPOSITE = {
 COMPOSITE.update({name: list(group) for name, group in synth.LORA_BACKWARD.items()})
 # Every frozen-weight a type at the 27B up-projection shape, one launch each.
 COMPOSITE["a_types_5120x17408"] = list(synth.TYPE_SWEEP)
+# ... and at m17408 k5120 n1024 (the 272 x 128 tile with loader waves).
+COMPOSITE["a_types_17408x5120"] = list(synth.TYPE_SWEEP_DOWN)
 # MUL_MAT_ID_BACK through q4_K experts: the up and down projections' input
 # gradients of one mixture-of-experts FFN (64 experts, 8 routed, 512 tokens).
 COMPOSITE["moe_back_q4_K"] = list(synth.MOE_WORKLOADS)

@@ -292,6 +292,17 @@ for _t in (F32, F16, BF16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K,
         _t, (5120, 17408, 1, 1), (1024, 17408, 1, 1), 80 + _t, 0.02 if _t in (F32, F16, BF16) else 1.0,
         "normal", "%s weight x f32 gradient, m 5120 k 17408 n 1024" % TYPE_NAMES[_t])
 WORKLOADS.update(TYPE_SWEEP)
+# ... and at the 27B down-projection's input-gradient shape (m 17408, k 5120,
+# n 1024), the 272 x 128 tile with loader waves.
+TYPE_SWEEP_DOWN = {}
+for _t in (F32, F16, BF16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K):
+    if _t == Q4_K:
+        TYPE_SWEEP_DOWN["q4_K_17408x5120"] = WORKLOADS["q4_K_17408x5120"]
+        continue
+    TYPE_SWEEP_DOWN["%s_17408x5120" % TYPE_NAMES[_t]] = (
+        _t, (17408, 5120, 1, 1), (1024, 5120, 1, 1), 120 + _t, 0.02 if _t in (F32, F16, BF16) else 1.0,
+        "normal", "%s weight x f32 gradient, m 17408 k 5120 n 1024" % TYPE_NAMES[_t])
+WORKLOADS.update(TYPE_SWEEP_DOWN)
 
 LORA_BACKWARD = {
     "lora_4B_linear_backward": lora_linear_backward("lora4B", 2560, 9216, 8, 512, 61),
