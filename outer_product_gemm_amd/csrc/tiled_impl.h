@@ -280,7 +280,10 @@ struct GatherLoaderKT {
             const int k = k0 + 4 * kq_of(g);
             floatx4 v = {0.f, 0.f, 0.f, 0.f};
             if (FULL) {
-                if (kGroups % T == 0 || g < kGroups) v = *(const floatx4 *)(col[j] + (int64_t)k * 4);
+                // K in range and 16-byte aligned; columns past the tile's
+                // slots (nullptr) stay zero
+                if ((kGroups % T == 0 || g < kGroups) && col[j] != nullptr)
+                    v = *(const floatx4 *)(col[j] + (int64_t)k * 4);
             } else if (col[j] != nullptr && k < K) {
                 const uint8_t *ptr = col[j] + (int64_t)k * 4;
                 if (vec && k + 3 < K) {
@@ -1260,9 +1263,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_id_kernel(IdProblem p, i
     const int fn_act = need < 0 ? 0 : need > FN ? FN : need;
     const bool a_vec_ok = (AT != OUTPROD_TYPE_F32 && AT != OUTPROD_TYPE_F16 && AT != OUTPROD_TYPE_BF16) ||
                           p.vec_a;
-    const bool full = m0 + BM <= M && cnt == BN && K % BK == 0 && a_vec_ok && p.vec_g;
+    // the expert's rows and K in range (the slot columns may stop short of
+    // BN: the gather loader leaves those zero)
+    const bool full = m0 + BM <= M && K % BK == 0 && a_vec_ok && p.vec_g;
     if (full)
-        C::template run<true>(la, lb, K, As, Bs, acc);
+        C::template run<true, true, true>(la, lb, K, As, Bs, acc, fn_act);
     else
         C::template run<false, true, true>(la, lb, K, As, Bs, acc, fn_act);
 
