@@ -71,20 +71,20 @@ PAGE_MS = {"q4_K_5120x17408": 91.0, "q4_K_17408x5120": 89.0, "q4_K_1536x1536": 2
 # scaled by the copy-kernel calibration), keyed by workload, valid only for
 # the kernel sources whose hash is recorded with it.
 MEASURED_TRAFFIC = {
-    # profiles/tiled_q4K_27B_lora_backward.md: launch A 378.5 MB, launch B 353.2 MB
-    "q4_K_27B_both": {"kernel_hash": "d92c4a81c0e80591", "bytes_per_launch": 365.88e6,
+    # profiles/tiled_q4K_27B_lora_backward.md: launch A 378.4 MB, launch B 353.2 MB
+    "q4_K_27B_both": {"kernel_hash": "bd4f5f101ce88df0", "bytes_per_launch": 365.82e6,
                       "profile": "profiles/tiled_q4K_27B_lora_backward.md"},
     # profiles/tiled_q4K_page_shapes.md: the four tiled launches (the m1536 split's
     # reduce kernel separate): 29.4 + 252.9 x 2 (m5120 k5120 and m5120 k17408, one
     # kernel group) + 353.2 MB
-    "q4_K_page_shapes": {"kernel_hash": "d92c4a81c0e80591", "bytes_per_launch": 222.12e6,
+    "q4_K_page_shapes": {"kernel_hash": "bd4f5f101ce88df0", "bytes_per_launch": 222.12e6,
                          "profile": "profiles/tiled_q4K_page_shapes.md"},
     # profiles/tiled_q8_0_5120.md
-    "q8_0_5120": {"kernel_hash": "d92c4a81c0e80591", "bytes_per_launch": 167.19e6,
+    "q8_0_5120": {"kernel_hash": "bd4f5f101ce88df0", "bytes_per_launch": 167.2e6,
                   "profile": "profiles/tiled_q8_0_5120.md"},
     # profiles/lora_linear_backward_4B_27B.md: the tiled launches (split dx_W main kernel
     # 68.4 MB and dx_A 5.6 MB); the split's reduce kernel is reported there separately
-    "lora_4B_linear_backward": {"kernel_hash": "d92c4a81c0e80591", "bytes_per_launch": 37.08e6,
+    "lora_4B_linear_backward": {"kernel_hash": "bd4f5f101ce88df0", "bytes_per_launch": 37.03e6,
                                 "profile": "profiles/lora_linear_backward_4B_27B.md"},
     # profiles/column_lora_rank_and_deltanet.md
     "lora_rank_r": {"kernel_hash": "d685f4d4c7ceb36c", "bytes_per_launch": 12.642e6,
@@ -96,7 +96,7 @@ MEASURED_TRAFFIC = {
     "deltanet_bcast": {"kernel_hash": "d685f4d4c7ceb36c", "bytes_per_launch": 7.45e6,
                        "profile": "profiles/column_lora_rank_and_deltanet.md"},
     # profiles/id_back_moe_q4_K.md: the grouped tiled launches (routing kernel separate)
-    "moe_back_q4_K": {"kernel_hash": "b3f2b6cb1bc9349e", "bytes_per_launch": 155.07e6,
+    "moe_back_q4_K": {"kernel_hash": "7766b790bf07e422", "bytes_per_launch": 155.01e6,
                       "profile": "profiles/id_back_moe_q4_K.md"},
 }
 
